@@ -1,0 +1,169 @@
+"""Python binding of libattn.so (exact tiled masked softmax attention, gfx950).
+
+Argument marshalling only: every function has the name, argument order and
+meaning of the C entry point declared in include/attn.h and forwards to it
+through ctypes.  Pointer arguments accept an integer device address, None, or
+any object with ``data_ptr()`` (a torch tensor).  ``stream`` defaults to the
+current torch stream when torch is importable, else the default stream.
+
+The library must be built (``python -m exact_tiled_softmax_amd.build``);
+importing this package raises if libattn.so is missing.  There is no fallback
+implementation.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
+    "ATTN_F32", "ATTN_F16", "ATTN_BF16", "AttnError", "Mask", "Dropout",
+    "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
+    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_status_string", "library_path", "lib",
+]
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_F32, ATTN_F16, ATTN_BF16 = range(3)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libattn.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        f"{library_path} is missing: build it with `python -m exact_tiled_softmax_amd.build` "
+        "(there is no fallback implementation)")
+
+lib = ctypes.CDLL(library_path)
+
+
+class Mask(ctypes.Structure):
+    """attn_mask_t: causal, window, block_mask (device ptr), block_q, block_k, dense_mask (device ptr)."""
+    _fields_ = [("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("block_mask", ctypes.c_void_p), ("block_q", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("dense_mask", ctypes.c_void_p)]
+
+
+class Dropout(ctypes.Structure):
+    """attn_dropout_t: rate (float), seed (uint64)."""
+    _fields_ = [("rate", ctypes.c_float), ("seed", ctypes.c_uint64)]
+
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_pm, _pd = ctypes.POINTER(Mask), ctypes.POINTER(Dropout)
+
+lib.attn_status_string.restype = ctypes.c_char_p
+lib.attn_status_string.argtypes = [_i]
+lib.attn_fwd.restype = _i
+lib.attn_fwd.argtypes = [_i] + [_i] * 7 + [_vp] * 3 + [_pm, _f, _i, _pd, _vp, _vp, _vp]
+lib.attn_bwd_workspace_size.restype = _sz
+lib.attn_bwd_workspace_size.argtypes = [_i] * 8
+lib.attn_bwd.restype = _i
+lib.attn_bwd.argtypes = ([_i] + [_i] * 7 + [_vp] * 6 + [_pm, _f, _i, _pd] + [_vp] * 3 + [_vp, _sz, _vp])
+lib.attn_sparse_fwd.restype = _i
+lib.attn_sparse_fwd.argtypes = [_i] + [_i] * 6 + [_vp] * 5 + [_f, _vp, _vp, _vp]
+lib.attn_sparse_bwd_workspace_size.restype = _sz
+lib.attn_sparse_bwd_workspace_size.argtypes = [_i] * 6
+lib.attn_sparse_bwd.restype = _i
+lib.attn_sparse_bwd.argtypes = ([_i] + [_i] * 6 + [_vp] * 5 + [_f] + [_vp] * 3 + [_vp] * 3 + [_vp, _sz, _vp])
+lib.attn_dropout_mask.restype = _i
+lib.attn_dropout_mask.argtypes = [_f, ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_string(status)} (status {status})")
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is not None:
+        return s if isinstance(s, int) else getattr(s, "cuda_stream", s)
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+    except Exception:  # pragma: no cover - torch without a GPU
+        pass
+    return None
+
+
+def _mask(m):
+    if m is None:
+        return None
+    if isinstance(m, Mask):
+        return ctypes.byref(m)
+    d = dict(m)
+    return ctypes.byref(Mask(int(d.get("causal", 0)), int(d.get("window", 0)), _ptr(d.get("block_mask")),
+                             int(d.get("block_q", 0)), int(d.get("block_k", 0)), _ptr(d.get("dense_mask"))))
+
+
+def _drop(d):
+    if d is None:
+        return None
+    if isinstance(d, Dropout):
+        return ctypes.byref(d)
+    rate, seed = d
+    return ctypes.byref(Dropout(float(rate), int(seed)))
+
+
+def _check(status, where, raise_on_error):
+    if raise_on_error and status != ATTN_OK:
+        raise AttnError(status, where)
+    return status
+
+
+def attn_status_string(status):
+    return lib.attn_status_string(int(status)).decode()
+
+
+def attn_fwd(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, mask, scale, block_b, dropout, Y, LSE,
+             stream=None, raise_on_error=True):
+    st = lib.attn_fwd(dt, B, H, H_kv, n_q, n_k, d, dv, _ptr(Q), _ptr(K), _ptr(V), _mask(mask),
+                      float(scale), int(block_b), _drop(dropout), _ptr(Y), _ptr(LSE), _stream(stream))
+    return _check(st, "attn_fwd", raise_on_error)
+
+
+def attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv):
+    return lib.attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv)
+
+
+def attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout,
+             dQ, dK, dV, workspace, workspace_bytes, stream=None, raise_on_error=True):
+    st = lib.attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, _ptr(Q), _ptr(K), _ptr(V), _ptr(Y), _ptr(LSE),
+                      _ptr(G), _mask(mask), float(scale), int(block_b), _drop(dropout), _ptr(dQ),
+                      _ptr(dK), _ptr(dV), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    return _check(st, "attn_bwd", raise_on_error)
+
+
+def attn_sparse_fwd(dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                    O, LSE, stream=None, raise_on_error=True):
+    st = lib.attn_sparse_fwd(dt, Tq, H, Tkv, d_qk, d_v, topk, _ptr(Q), _ptr(KV), _ptr(topk_idx),
+                             _ptr(topk_length), _ptr(attn_sink), float(scale), _ptr(O), _ptr(LSE),
+                             _stream(stream))
+    return _check(st, "attn_sparse_fwd", raise_on_error)
+
+
+def attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk):
+    return lib.attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk)
+
+
+def attn_sparse_bwd(dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                    O, LSE, dO, dQ, dKV, dSink, workspace, workspace_bytes, stream=None,
+                    raise_on_error=True):
+    st = lib.attn_sparse_bwd(dt, Tq, H, Tkv, d_qk, d_v, topk, _ptr(Q), _ptr(KV), _ptr(topk_idx),
+                             _ptr(topk_length), _ptr(attn_sink), float(scale), _ptr(O), _ptr(LSE),
+                             _ptr(dO), _ptr(dQ), _ptr(dKV), _ptr(dSink), _ptr(workspace),
+                             int(workspace_bytes), _stream(stream))
+    return _check(st, "attn_sparse_bwd", raise_on_error)
+
+
+def attn_dropout_mask(rate, seed, B, H, n_q, n_k, xi, stream=None, raise_on_error=True):
+    st = lib.attn_dropout_mask(float(rate), int(seed), B, H, n_q, n_k, _ptr(xi), _stream(stream))
+    return _check(st, "attn_dropout_mask", raise_on_error)

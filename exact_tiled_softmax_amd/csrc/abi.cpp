@@ -1,0 +1,229 @@
+// C-ABI entry points of libattn.so: host-side validation and dispatch.
+// Every check happens before any launch; on failure nothing is launched and
+// no output is written.  The declarations and their contracts are in
+// include/attn.h.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "params.hpp"
+
+using namespace ets;
+
+namespace {
+
+constexpr int kMaxF32Width = 128;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool bad_dims(std::initializer_list<long long> v) {
+  for (long long x : v)
+    if (x < 1 || x > (1LL << 30)) return true;
+  return false;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shared validation of the dense forward/backward arguments.
+attn_status check_dense(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                        const attn_mask_t* mask, float scale, int block_b,
+                        const attn_dropout_t* drop) {
+  if (dt != ATTN_F32 && dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (bad_dims({B, H, H_kv, n_q, n_k, d, dv})) return ATTN_ERR_INVALID_ARG;
+  if (H % H_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if ((long long)B * H * n_q > (1LL << 31) - 1 || (long long)B * H_kv * n_k > (1LL << 31) - 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+  if (block_b < 0) return ATTN_ERR_INVALID_ARG;
+  if (mask) {
+    if (mask->causal && n_q != n_k) return ATTN_ERR_INVALID_ARG;
+    if (mask->window < 0) return ATTN_ERR_INVALID_ARG;
+    if (mask->block_mask && (mask->block_q < 1 || mask->block_k < 1)) return ATTN_ERR_INVALID_ARG;
+  }
+  if (drop) {
+    if (!std::isfinite(drop->rate) || drop->rate < 0.f || drop->rate >= 1.f) return ATTN_ERR_INVALID_ARG;
+  }
+  if (dt == ATTN_F32) {
+    if (d > kMaxF32Width || dv > kMaxF32Width) return ATTN_ERR_UNSUPPORTED;
+  } else {
+    if (!dense_mfma_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+    if (block_b != 0 && block_b != 64) return ATTN_ERR_UNSUPPORTED;
+  }
+  return ATTN_OK;
+}
+
+void fill_dense(DenseArgs& a, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                const attn_mask_t* mask, float scale, int block_b, const attn_dropout_t* drop) {
+  std::memset(&a, 0, sizeof(a));
+  a.B = B; a.H = H; a.Hkv = H_kv; a.nq = n_q; a.nk = n_k; a.d = d; a.dv = dv;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.block_b = (dt == ATTN_F32) ? (block_b > 0 ? block_b : 64) : 64;
+  if (mask) {
+    a.mask.causal = mask->causal != 0;
+    a.mask.window = mask->window;
+    a.mask.block_mask = mask->block_mask;
+    a.mask.bq = mask->block_mask ? mask->block_q : 1;
+    a.mask.bk = mask->block_mask ? mask->block_k : 1;
+    a.mask.nbk = mask->block_mask ? (n_k + mask->block_k - 1) / mask->block_k : 0;
+    a.mask.dense_mask = mask->dense_mask;
+  }
+  if (drop && drop->rate > 0.f) {
+    const double r = (double)drop->rate;
+    a.drop.enabled = 1;
+    a.drop.threshold = (uint32_t)std::floor(r * 4294967296.0);
+    a.drop.seed_lo = (uint32_t)(drop->seed & 0xffffffffu);
+    a.drop.seed_hi = (uint32_t)(drop->seed >> 32);
+    a.drop.inv_keep = (float)(1.0 / (1.0 - r));
+  }
+}
+
+size_t elem_bytes(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+attn_status attn_fwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                     const void* Q, const void* K, const void* V, const attn_mask_t* mask,
+                     float scale, int block_b, const attn_dropout_t* dropout, void* Y, float* LSE,
+                     void* stream) {
+  attn_status st = check_dense(dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
+  if (st != ATTN_OK) return st;
+  if (!Q || !K || !V || !Y || !LSE) return ATTN_ERR_INVALID_ARG;
+  const size_t al = dt == ATTN_F32 ? 4 : 16;
+  if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(Y, al) || !aligned(LSE, 4))
+    return ATTN_ERR_INVALID_ARG;
+  DenseArgs a;
+  fill_dense(a, dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
+  a.Q = Q; a.K = K; a.V = V; a.out_Y = Y; a.LSE = LSE;
+  const int rc = dt == ATTN_F32 ? launch_dense_fwd_f32(a, stream)
+                                : launch_dense_fwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
+                               int dv) {
+  (void)dt; (void)H_kv; (void)n_k; (void)d; (void)dv;
+  if (bad_dims({B, H, n_q})) return 0;
+  return round_up((size_t)B * H * n_q * sizeof(float));
+}
+
+attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                     const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
+                     const void* G, const attn_mask_t* mask, float scale, int block_b,
+                     const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_dense(dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
+  if (st != ATTN_OK) return st;
+  if (!Q || !K || !V || !Y || !LSE || !G || !dQ || !dK || !dV) return ATTN_ERR_INVALID_ARG;
+  const size_t al = dt == ATTN_F32 ? 4 : 16;
+  for (const void* p : {Q, K, V, Y, G, (const void*)dQ, (const void*)dK, (const void*)dV})
+    if (!aligned(p, al)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(LSE, 4)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  DenseArgs a;
+  fill_dense(a, dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
+  a.Q = Q; a.K = K; a.V = V; a.Y = Y; a.LSE = (float*)LSE; a.G = G;
+  a.dQ = dQ; a.dK = dK; a.dV = dV; a.Dws = (float*)workspace;
+  const int rc = dt == ATTN_F32 ? launch_dense_bwd_f32(a, stream)
+                                : launch_dense_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+static attn_status check_sparse(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                                float scale) {
+  if (dt != ATTN_F16 && dt != ATTN_BF16) return dt == ATTN_F32 ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG;
+  if (bad_dims({Tq, H, Tkv, d_qk, d_v, topk})) return ATTN_ERR_INVALID_ARG;
+  if (d_v > d_qk) return ATTN_ERR_INVALID_ARG;
+  if ((long long)Tq * topk > (1LL << 31) - 1 || (long long)Tq * H > (1LL << 31) - 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+  if (!sparse_supported(H, d_qk, d_v)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+static void fill_sparse(SparseArgs& a, int Tq, int H, int Tkv, int d_qk, int d_v, int topk, float scale) {
+  std::memset(&a, 0, sizeof(a));
+  a.Tq = Tq; a.H = H; a.Tkv = Tkv; a.dqk = d_qk; a.dv = d_v; a.topk = topk;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+}
+
+attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                            const void* Q, const void* KV, const int32_t* topk_idx,
+                            const int32_t* topk_length, const float* attn_sink, float scale,
+                            void* O, float* LSE, void* stream) {
+  attn_status st = check_sparse(dt, Tq, H, Tkv, d_qk, d_v, topk, scale);
+  if (st != ATTN_OK) return st;
+  if (!Q || !KV || !topk_idx || !O || !LSE) return ATTN_ERR_INVALID_ARG;
+  for (const void* p : {Q, KV, (const void*)O})
+    if (!aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(topk_idx, 4) || !aligned(LSE, 4) || (topk_length && !aligned(topk_length, 4)) ||
+      (attn_sink && !aligned(attn_sink, 4)))
+    return ATTN_ERR_INVALID_ARG;
+  SparseArgs a;
+  fill_sparse(a, Tq, H, Tkv, d_qk, d_v, topk, scale);
+  a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
+  a.O = O; a.LSE = LSE;
+  const int rc = launch_sparse_fwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk) {
+  (void)d_v; (void)topk;
+  if (bad_dims({Tq, H, Tkv, d_qk})) return 0;
+  return round_up((size_t)Tq * H * sizeof(float)) + round_up((size_t)Tkv * d_qk * sizeof(float));
+}
+
+attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                            const void* Q, const void* KV, const int32_t* topk_idx,
+                            const int32_t* topk_length, const float* attn_sink, float scale,
+                            const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                            float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_sparse(dt, Tq, H, Tkv, d_qk, d_v, topk, scale);
+  if (st != ATTN_OK) return st;
+  if (!Q || !KV || !topk_idx || !O || !LSE || !dO || !dQ || !dKV) return ATTN_ERR_INVALID_ARG;
+  if (attn_sink && !dSink) return ATTN_ERR_INVALID_ARG;
+  for (const void* p : {Q, KV, O, dO, (const void*)dQ, (const void*)dKV})
+    if (!aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(topk_idx, 4) || !aligned(LSE, 4) || (topk_length && !aligned(topk_length, 4)) ||
+      (attn_sink && !aligned(attn_sink, 4)) || (dSink && !aligned(dSink, 4)))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return ATTN_ERR_WORKSPACE;
+  SparseArgs a;
+  fill_sparse(a, Tq, H, Tkv, d_qk, d_v, topk, scale);
+  a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
+  a.O = (void*)O; a.LSE = (float*)LSE; a.dO = dO; a.dQ = dQ; a.dKV = dKV; a.dSink = dSink;
+  a.Dws = (float*)workspace;
+  a.dKVws = (float*)((char*)workspace + round_up((size_t)Tq * H * sizeof(float)));
+  const int rc = launch_sparse_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_dropout_mask(float rate, uint64_t seed, int B, int H, int n_q, int n_k,
+                              uint8_t* xi, void* stream) {
+  if (bad_dims({B, H, n_q, n_k}) || !xi) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(rate) || rate < 0.f || rate >= 1.f) return ATTN_ERR_INVALID_ARG;
+  if ((long long)B * H * n_q * (long long)n_k > (1LL << 40)) return ATTN_ERR_INVALID_ARG;
+  attn_dropout_t d{rate, seed};
+  DenseArgs a;
+  fill_dense(a, ATTN_F32, B, H, H, n_q, n_k, 1, 1, nullptr, 1.f, 0, &d);
+  const int rc = launch_dropout_mask(a.drop, B, H, n_q, n_k, xi, stream);
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Device helpers for the gfx950 (CDNA4) attention kernels: element types and
+// MFMA wrappers, the swizzled LDS tile format, cross-half lane exchange,
+// Philox4x32-10 and the allowed-set tests.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "params.hpp"
+
+namespace ets {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+#define ETS_LDS __attribute__((address_space(3)))
+
+// ------------------------------------------------------------ element types
+// Storage is 16-bit in memory; MFMA operands are 8 elements (16 bytes) per lane.
+
+struct BF16 {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // two floats -> packed pair, round to nearest even
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    f32x2 v = {x, y};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+};
+
+struct F16 {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    f32x2 v = {x, y};
+    f16x2 r = __builtin_convertvector(v, f16x2);
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
+template <class E>
+__device__ __forceinline__ typename E::vec8 as_vec8(u32x4 u) {
+  return __builtin_bit_cast(typename E::vec8, u);
+}
+
+// ------------------------------------------------------------ LDS tile format
+// A tile is row-major with a fixed byte stride per row; its 16-byte chunks are
+// XOR-swizzled by swz(row) within each group of 8 chunks.  The swizzle makes
+// both access patterns of the kernels conflict-free:
+//   * 16-byte reads of one chunk column by 8 consecutive rows (MFMA operand
+//     rows), and
+//   * transpose reads, where 16 lanes read 4 consecutive rows (starting at a
+//     multiple of 4) x 32 contiguous bytes.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// byte offset of element (row, col) of a 16-bit tile
+__device__ __forceinline__ int toff(int row, int col, int rowbytes) {
+  return row * rowbytes + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ u32x4 lds_b128(const char ETS_LDS* base, int off) {
+  return *(const u32x4 ETS_LDS*)(base + off);
+}
+
+__device__ __forceinline__ void lds_st128(char ETS_LDS* base, int off, u32x4 v) {
+  *(u32x4 ETS_LDS*)(base + off) = v;
+}
+
+// Transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// supplies the address of 4 consecutive elements (row r0 + i/4, cols
+// c0 + 4*(i%4) .. +3); it receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ s16x4 lds_tr4(const char ETS_LDS* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 ETS_LDS*)(base + off));
+}
+
+// An MFMA operand holding 8 elements of one column (the "m" or "n" index
+// col0 + lane%32 for 32x32 shapes) along 8 rows: the lane's k-slots 0..3 are
+// rows r0 .. r0+3 and slots 4..7 are rows r1 .. r1+3.
+__device__ __forceinline__ u32x4 lds_tr8(const char ETS_LDS* base, int r0, int r1, int col0,
+                                         int rowbytes, int lane) {
+  const int i = lane & 15;
+  const int col = col0 + 4 * (i & 3);
+  s16x4 a = lds_tr4(base, toff(r0 + (i >> 2), col, rowbytes));
+  s16x4 b = lds_tr4(base, toff(r1 + (i >> 2), col, rowbytes));
+  s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(u32x4, v);
+}
+
+// ------------------------------------------------------------ lane exchange
+// permlane32_swap(x, x) hands every lane the value of lane (l ^ 32) in one of
+// its two results; combining both gives a full cross-half reduction.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ------------------------------------------------------------ Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3"
+// (SC'11): ten rounds of the Philox S-box on a 4x32-bit counter, with the
+// 2x32-bit key bumped by the Weyl increments between rounds.
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
+    const uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// Keep bits of dropout for keys j0 .. j0+3 (j0 % 4 == 0) of query row i in
+// lane (b*H + h): counter (j0/4, i, lane, 0), word r decides key j0 + r.
+__device__ __forceinline__ unsigned keep4(const DropArgs& d, int lane_bh, int i, int j0) {
+  U4 w = philox4x32_10((uint32_t)(j0 >> 2), (uint32_t)i, (uint32_t)lane_bh, 0u, d.seed_lo, d.seed_hi);
+  return (unsigned)(w.x >= d.threshold) | ((unsigned)(w.y >= d.threshold) << 1) |
+         ((unsigned)(w.z >= d.threshold) << 2) | ((unsigned)(w.w >= d.threshold) << 3);
+}
+
+// ------------------------------------------------------------ allowed sets
+// Allowed bits of keys j0 .. j0+3 for query row i (bit r <-> key j0 + r).
+__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk) {
+  if (i >= nq) return 0u;
+  unsigned bits = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = j0 + r;
+    bool ok = j < nk;
+    if (m.causal) ok = ok && (j <= i);
+    if (m.window > 0) ok = ok && (i - j < m.window);
+    if (ok && m.block_mask) ok = m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] != 0;
+    if (ok && m.dense_mask) ok = m.dense_mask[(size_t)i * nk + j] != 0;
+    bits |= (unsigned)ok << r;
+  }
+  return bits;
+}
+
+enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2 };
+
+// Classify the rectangle of query rows [ia, ib] x keys [ja, jb] (inclusive;
+// jb may run past nk for a ragged last tile).  Uniform across the wave.
+__device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int ja, int jb, int nq, int nk) {
+  if (ia >= nq || ja >= nk) return kEmpty;
+  if (ib >= nq) ib = nq - 1;
+  int cls = (jb >= nk) ? kPartial : kFull;
+  if (jb >= nk) jb = nk - 1;
+  if (m.causal) {
+    if (ja > ib) return kEmpty;
+    if (jb > ia) cls = kPartial;
+  }
+  if (m.window > 0) {
+    if (ia - jb >= m.window) return kEmpty;
+    if (ib - ja >= m.window) cls = kPartial;
+  }
+  if (m.block_mask) {
+    const int r0 = ia / m.bq, r1 = ib / m.bq, c0 = ja / m.bk, c1 = jb / m.bk;
+    if ((r1 - r0 + 1) * (c1 - c0 + 1) > 64) {
+      cls = kPartial;
+    } else {
+      int ones = 0, tot = 0;
+      for (int r = r0; r <= r1; ++r)
+        for (int c = c0; c <= c1; ++c) {
+          ones += m.block_mask[(size_t)r * m.nbk + c] != 0;
+          ++tot;
+        }
+      if (ones == 0) return kEmpty;
+      if (ones != tot) cls = kPartial;
+    }
+  }
+  if (m.dense_mask) cls = kPartial;
+  return cls;
+}
+
+}  // namespace ets

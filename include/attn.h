@@ -1,0 +1,206 @@
+/*
+ * Exact tiled masked softmax attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Every entry point validates its arguments on the host
+ * before anything is launched; on an error nothing is launched and no output
+ * is touched.  Kernels run asynchronously on the caller's stream; the library
+ * allocates no memory, keeps no state between calls and is re-entrant.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are device pointers allocated and owned by the caller.
+ *     Tensors are dense and row-major with the feature dimension contiguous.
+ *     16-bit tensors must be 16-byte aligned.
+ *   - Outputs (Y, LSE, dQ, dK, dV, O, dKV, dSink) are overwritten, never
+ *     accumulated into.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ *   - A failed kernel launch returns ATTN_ERR_HIP.
+ *   - Non-finite input values are not checked; they propagate.
+ *
+ * Sources.  The operation is defined on these pages:
+ *   [P1] alphabetamath.cc, "Tiled attention and its recomputed reverse pass
+ *        are exact" (the summary invariant, the empty state, exactness of the
+ *        forward row and of the reverse updates);
+ *   [P2] alphabetamath.cc, "Exact tiled attention and memory-aware
+ *        differentiation -- Examples" (worked examples, inverted dropout);
+ *   [P3] intale.github.io, practical LLM in Rust, ch. 19 "Online tiled
+ *        attention" (update rule, reverse formulas, grouped heads);
+ *   [P5] icavan.github.io, "DeepSeek Sparse Attention Forward and Backward"
+ *        (shared-KV top-k sparse attention with a sink).
+ */
+#ifndef EXACT_TILED_SOFTMAX_ATTN_H
+#define EXACT_TILED_SOFTMAX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment, scale, rate or mask */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size() */
+  ATTN_ERR_HIP = 4          /* a HIP launch failed */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
+
+/*
+ * The allowed-key sets A_i of [P1]: allowed(i, j) is the AND of every
+ * enabled part; with no part enabled every key is allowed.
+ *   causal      nonzero: j <= i (requires n_q == n_k)
+ *   window      > 0: i - j < window (a look-back window; with causal the
+ *               window holds `window` keys including key i); 0: off
+ *   block_mask  device pointer to uint8 [ceil(n_q/block_q)][ceil(n_k/block_k)],
+ *               shared by all batches and heads; key j is allowed for row i
+ *               only if block_mask[i/block_q][j/block_k] != 0; NULL: off
+ *   dense_mask  device pointer to uint8 [n_q][n_k], shared by all batches and
+ *               heads; NULL: off
+ * A NULL attn_mask_t* means every key is allowed.  A row whose allowed set is
+ * empty gets Y = 0 and LSE = -inf and contributes nothing to any gradient
+ * (the convention [P3] uses for query rows without keys).
+ */
+typedef struct {
+  int32_t causal;
+  int32_t window;
+  const uint8_t* block_mask;
+  int32_t block_q, block_k;
+  const uint8_t* dense_mask;
+} attn_mask_t;
+
+/*
+ * Inverted dropout ([P2], "A different dropout mask changes the reverse
+ * result"): each attention weight p_ij is multiplied by xi_ij / (1 - rate).
+ * xi is regenerated, never stored: with Philox4x32-10 (Salmon et al., SC'11),
+ * key = (seed mod 2^32, seed div 2^32) and counter = (j div 4, i, b*H + h, 0),
+ * output word (j mod 4) is u and xi_ij = 0 iff u < floor(rate * 2^32), where
+ * rate is widened to double.  The forward and reverse passes draw identical
+ * xi.  The normaliser l_i and the LSE use the undropped weights.
+ * NULL or rate == 0: no dropout.  rate must lie in [0, 1).
+ */
+typedef struct {
+  float rate;
+  uint64_t seed;
+} attn_dropout_t;
+
+/*
+ * attn_fwd -- exact tiled masked attention forward ([P1] paragraphs 1-2,
+ * [P3] "Rescale earlier mass before adding a new tile").
+ *
+ *   Y_i   = sum_{j in A_i} e^{s_ij} V_j / sum_{j in A_i} e^{s_ij},
+ *   s_ij  = scale * sum_r Q_ir K_jr,   LSE_i = ln sum_{j in A_i} e^{s_ij}.
+ *
+ * Keys are streamed in blocks with the running summary (m, l, z) started in
+ * the empty state; empty allowed blocks leave it unchanged; the full score grid
+ * is never stored.
+ *
+ *   dt        ATTN_F32, ATTN_F16 or ATTN_BF16 (Q, K, V, Y); LSE is always fp32
+ *   Q         [B][H][n_q][d]
+ *   K         [B][H_kv][n_k][d]      query head h reads K/V head h / (H / H_kv)
+ *   V         [B][H_kv][n_k][dv]
+ *   mask      allowed sets (see attn_mask_t), may be NULL
+ *   scale     c >= 0, finite
+ *   block_b   key-block size b: fp32 honours any b >= 1 exactly; the bf16/fp16
+ *             kernels use b = 64 and accept 0 or 64; 0 = the kernel default
+ *   dropout   may be NULL
+ *   Y         [B][H][n_q][dv] output, same dtype as Q
+ *   LSE       [B][H][n_q] fp32 output (natural log)
+ * Shapes: fp32 needs d, dv <= 128; bf16/fp16 need d == dv in {64, 128}.
+ */
+attn_status attn_fwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                     const void* Q, const void* K, const void* V, const attn_mask_t* mask,
+                     float scale, int block_b, const attn_dropout_t* dropout,
+                     void* Y, float* LSE, void* stream);
+
+/* Bytes of device workspace attn_bwd needs (fp32 D_i for every query row). */
+size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
+                               int dv);
+
+/*
+ * attn_bwd -- block-recomputed reverse pass ([P1] paragraphs 4-6, [P3]
+ * "Reconstruct probabilities when a gradient needs them"): the exact gradient
+ * of Phi = sum_i sum_a G_ia Y_ia,
+ *
+ *   D_i = sum_a G_ia Y_ia,   p_ij = e^{s_ij - LSE_i} on A_i,
+ *   gamma_ij = p_ij (kappa_ij G_i . V_j - D_i),  kappa = xi / (1 - rate),
+ *   dQ_i = c sum_j gamma_ij K_j,  dK_j = c sum_i gamma_ij Q_i,
+ *   dV_j = sum_i p_ij kappa_ij G_i,
+ *
+ * with dK, dV of all query heads of a group summed into the shared head.
+ * Arguments as attn_fwd, plus
+ *   Y, LSE    exactly what attn_fwd wrote for the same inputs
+ *   G         [B][H][n_q][dv] upstream gradient
+ *   dQ, dK, dV  outputs shaped like Q, K, V
+ *   workspace   device memory of at least attn_bwd_workspace_size() bytes,
+ *               16-byte aligned; contents on entry are ignored
+ */
+attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                     const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
+                     const void* G, const attn_mask_t* mask, float scale, int block_b,
+                     const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_sparse_fwd -- shared-KV top-k sparse attention with sink ([P5]
+ * sections 1, 2 and 7.1).  For token t and head h, with the selected rows
+ * I = topk_idx[t][0 : L_t] (L_t = topk_length[t], or topk when NULL):
+ *
+ *   s_u = scale * KV[I_u][0:d_qk] . Q[t][h],   Z = e^{z_h} + sum_u e^{s_u},
+ *   O[t][h] = sum_u (e^{s_u} / Z) KV[I_u][0:d_v],   LSE[t][h] = ln Z,
+ *
+ * where z_h = attn_sink[h] (no sink when attn_sink is NULL: z = -inf).  The
+ * exported LSE is sink-inclusive.
+ *   dt           ATTN_BF16 or ATTN_F16
+ *   Q            [Tq][H][d_qk];  KV [Tkv][d_qk] (the value is its first d_v columns)
+ *   topk_idx     int32 [Tq][topk]; entries < L_t must lie in [0, Tkv), the
+ *                rest are never read; duplicates are allowed
+ *   topk_length  int32 [Tq], values in [0, topk], or NULL
+ *   attn_sink    fp32 [H] or NULL
+ *   O            [Tq][H][d_v] output;  LSE fp32 [Tq][H] output
+ * Shapes: H == 64, d_qk == 576, d_v == 512.  A token with no selected row
+ * gets O = 0 and LSE = z_h (-inf without a sink).
+ */
+attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                            const void* Q, const void* KV, const int32_t* topk_idx,
+                            const int32_t* topk_length, const float* attn_sink, float scale,
+                            void* O, float* LSE, void* stream);
+
+/* Bytes of device workspace attn_sparse_bwd needs (fp32 D per (token, head)
+ * and an fp32 [Tkv][d_qk] dKV accumulator). */
+size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk);
+
+/*
+ * attn_sparse_bwd -- gradients of the sparse operator ([P5] sections 3 and
+ * 8):  D = dO . O;  dS_u = p_u (dO . v_u - D);  dQ = scale sum_u dS_u k_u;
+ * dKV[I_u][:] += scale dS_u q and dKV[I_u][0:d_v] += p_u dO (the tied K/V row),
+ * summed over every token and head in fp32 and rounded once;
+ * dSink[h] = -sum_t p_sink(t, h) D(t, h).
+ * Arguments as attn_sparse_fwd, plus O and LSE as attn_sparse_fwd wrote them,
+ * dO [Tq][H][d_v], outputs dQ [Tq][H][d_qk], dKV [Tkv][d_qk] and dSink fp32 [H]
+ * (required iff attn_sink is not NULL), and the workspace.  dKV is summed with
+ * fp32 atomics, so its bits may differ between runs.
+ */
+attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                            const void* Q, const void* KV, const int32_t* topk_idx,
+                            const int32_t* topk_length, const float* attn_sink, float scale,
+                            const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                            float* dSink, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_dropout_mask -- writes the dropout realisation xi that attn_fwd and
+ * attn_bwd use (see attn_dropout_t) as uint8 [B][H][n_q][n_k] (1 = kept), for
+ * inspection and tests.
+ */
+attn_status attn_dropout_mask(float rate, uint64_t seed, int B, int H, int n_q, int n_k,
+                              uint8_t* xi, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(attn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TILED_SOFTMAX_ATTN_H */

@@ -1,0 +1,96 @@
+"""Device plumbing for the GPU tests: torch for memory, the C ABI for compute.
+
+Inputs come from ``workloads`` (seeded, rounded to the storage dtype); the
+oracle receives the same values widened to float64.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+
+DT = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    return torch
+
+
+def to_dev(storage, dtype):
+    torch = torch_cuda()
+    a = np.ascontiguousarray(storage)
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16))
+    else:
+        t = torch.from_numpy(a)
+    return t.to("cuda")
+
+
+def empty(shape, dtype):
+    torch = torch_cuda()
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.int16}[dtype]
+    return torch.full(shape, 0, dtype=tdt, device="cuda")
+
+
+def from_dev(t, dtype):
+    a = t.detach().cpu().numpy()
+    if dtype == "bf16":
+        return workloads.bf16_bits_to_f64(a.view(np.uint16))
+    return a.astype(np.float64)
+
+
+def rel_fro(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
+
+
+def lse_err(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    both_inf = np.isneginf(x) & np.isneginf(ref)
+    if np.any(np.isneginf(x) != np.isneginf(ref)):
+        return float("inf")
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, x - ref)
+    return float(np.max(np.abs(diff), initial=0.0))
+
+
+def mask_arg(causal=False, window=0, block_mask=None, block_q=64, block_k=64, dense_mask=None):
+    """attn_mask_t fields as a dict of device objects (kept alive by the caller)."""
+    d = {"causal": int(causal), "window": int(window), "block_q": block_q, "block_k": block_k}
+    if block_mask is not None:
+        d["block_mask"] = to_dev(np.asarray(block_mask, np.uint8), "u8")
+    if dense_mask is not None:
+        d["dense_mask"] = to_dev(np.asarray(dense_mask, np.uint8), "u8")
+    return d
+
+
+def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=True):
+    """Run attn_fwd (and attn_bwd) on storage arrays; return float64 results."""
+    import exact_tiled_softmax_amd as ets
+    torch = torch_cuda()
+    B, H, n_q, d = Q.shape
+    H_kv, n_k, dv = K.shape[1], K.shape[2], V.shape[3]
+    dq, dk, dvv = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    Y = empty((B, H, n_q, dv), dtype)
+    LSE = torch.zeros((B, H, n_q), dtype=torch.float32, device="cuda")
+    dt = DT[dtype]
+    ets.attn_fwd(dt, B, H, H_kv, n_q, n_k, d, dv, dq, dk, dvv, mask, scale, block_b, dropout, Y, LSE)
+    out = {"Y": Y, "LSE": LSE}
+    if backward:
+        dg = to_dev(G, dtype)
+        dQ, dK, dV = empty(Q.shape, dtype), empty(K.shape, dtype), empty(V.shape, dtype)
+        ws_bytes = ets.attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        ets.attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, dq, dk, dvv, Y, LSE, dg, mask, scale, block_b,
+                     dropout, dQ, dK, dV, ws, ws_bytes)
+        out.update(dQ=dQ, dK=dK, dV=dV)
+    torch.cuda.synchronize()
+    res = {k: (from_dev(v, dtype) if k != "LSE" else v.cpu().numpy().astype(np.float64)) for k, v in out.items()}
+    res["_dev"] = out
+    return res
