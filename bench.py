@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled masked softmax attention on one MI355X.
+
+One step = one pass of the whole hot path over one batch: attn_fwd followed by
+the three backward launches (prepass, dK/dV, dQ) on the same stream.  Inputs
+are seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Flops are algorithmic: only allowed (query, key) pairs count.  Per pair the
+forward does 2d + 2dv flops (S = c Q K^T, then P V) and the backward 6d + 4dv
+(S recompute, dP = G V^T, dV, dK, dQ).  The dK/dV kernel accounts for
+4d + 4dv of them and the dQ kernel for 2d (its S and dP recomputations are
+redundant work, not counted).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA peaks (fp32: vector)
+PEAK_HBM_GBS = 8000.0
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak (causal, seq 2048, d=128)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dense_pairs(w, block_mask):
+    """|A| = number of allowed (query, key) pairs per (batch, head) lane, counted on the host."""
+    n = w.n
+    i = np.arange(n)[:, None]
+    total = 0
+    step = max(1, (1 << 22) // n)
+    for r0 in range(0, n, step):
+        ii = i[r0:r0 + step]
+        j = np.arange(n)[None, :]
+        a = np.ones((ii.shape[0], n), bool)
+        if w.causal:
+            a &= j <= ii
+        if w.window > 0:
+            a &= (ii - j) < w.window
+        if block_mask is not None:
+            a &= block_mask[ii // w.mask_tile, j // w.mask_tile] != 0
+        total += int(a.sum())
+    return total
+
+
+def cpu_baseline_dense(w, arr, block_mask, budget_s=12.0):
+    """The fp64 oracle, untouched, timed on the host on a bounded sample of
+    (batch, head) lanes of the same workload."""
+    from oracle import dense
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    allowed = dense.Allowed(w.n, w.n, causal=w.causal, window=w.window, block_mask=block_mask,
+                            block_q=w.mask_tile, block_k=w.mask_tile)
+    drop = dense.Dropout(float(np.float32(w.rho)), seed=w.drop_seed) if w.rho > 0 else None
+    per_pair = (2 * w.d + 2 * w.dv) + (6 * w.d + 4 * w.dv)
+    pairs_lane = dense_pairs(w, block_mask)
+    lanes, t_total = 0, 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            t0 = time.perf_counter()
+            dense.forward_rows(arr["Q64"], arr["K64"], arr["V64"], allowed, w.c, b, h, np.arange(w.n), drop)
+            dense.vjp_lane(arr["Q64"], arr["K64"], arr["V64"], allowed, w.c, arr["G64"], b, h, drop)
+            t_total += time.perf_counter() - t0
+            lanes += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    tflops = lanes * pairs_lane * per_pair / t_total / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 forward + VJP of {lanes} of {w.B * w.H} (batch, head) lanes "
+                      f"({lanes * pairs_lane} allowed pairs) in {t_total:.1f} s"}
+
+
+def bench_dense(w, args):
+    import torch
+    import exact_tiled_softmax_amd as ets
+    from tests import gpu_helpers as gh
+
+    arr = workloads.dense_arrays(w)
+    block_mask = arr["block_mask"]
+    dt = DTYPE_CODE[w.dtype]
+    Q, K, V, G = (gh.to_dev(arr[k], w.dtype) for k in ("Q", "K", "V", "G"))
+    Y = gh.empty((w.B, w.H, w.n, w.dv), w.dtype)
+    LSE = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device="cuda")
+    dQ, dK, dV = gh.empty(Q.shape, w.dtype), gh.empty(K.shape, w.dtype), gh.empty(V.shape, w.dtype)
+    ws_bytes = ets.attn_bwd_workspace_size(dt, w.B, w.H, w.H_kv, w.n, w.n, w.d, w.dv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    mask = {"causal": int(w.causal), "window": w.window, "block_q": w.mask_tile, "block_k": w.mask_tile}
+    if block_mask is not None:
+        mask["block_mask"] = gh.to_dev(block_mask, "u8")
+    drop = (w.rho, w.drop_seed) if w.rho > 0 else None
+    shape = (dt, w.B, w.H, w.H_kv, w.n, w.n, w.d, w.dv)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        ets.attn_fwd(*shape, Q, K, V, mask, w.c, w.block_b, drop, Y, LSE, stream=stream)
+
+    def bwd(phase):
+        ets.attn_bwd_phase(phase, *shape, Q, K, V, Y, LSE, G, mask, w.c, w.block_b, drop, dQ, dK, dV, ws,
+                           ws_bytes, stream=stream)
+
+    names = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
+    calls = [fwd, lambda: bwd(1), lambda: bwd(2), lambda: bwd(4)]
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for k, c in enumerate(calls):
+            c()
+            ev[s][k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = {n: float(np.mean([ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(args.steps)]))
+               for k, n in enumerate(names)}
+
+    pairs = dense_pairs(w, block_mask) * w.B * w.H
+    d, dv = w.d, w.dv
+    flops = {"fwd": pairs * (2 * d + 2 * dv), "bwd_dkdv": pairs * (4 * d + 4 * dv), "bwd_dq": pairs * 2 * d}
+    f_fwd, f_bwd = flops["fwd"], flops["bwd_dkdv"] + flops["bwd_dq"]
+    peak = PEAK_TFLOPS[w.dtype]
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    prep_bytes = 2 * w.B * w.H * w.n * w.dv * (2 if w.dtype != "f32" else 4) + 4 * w.B * w.H * w.n
+    kernels = {}
+    for n in names:
+        if n == "bwd_prep":
+            gbs = prep_bytes / (kern_ms[n] * 1e-3) / 1e9
+            kernels[n] = {"ms": kern_ms[n], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        else:
+            tf = flops[n] / (kern_ms[n] * 1e-3) / 1e12
+            kernels[n] = {"ms": kern_ms[n], "TFLOP/s": tf, "frac_peak": tf / peak}
+    dom = max(["fwd", "bwd_dkdv", "bwd_dq"], key=lambda n: kern_ms[n])
+    roofline = {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": peak, "unit": "TFLOP/s",
+                "frac": kernels[dom]["TFLOP/s"] / peak, "traffic": None, "kernel": dom,
+                "flops_per_launch": flops[dom]}
+    fwd_tf = f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
+    bwd_ms = kern_ms["bwd_prep"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), workloads module)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "kv_heads": w.H_kv, "seq_len": w.n,
+                   "head_dim": w.d, "causal": w.causal, "window": w.window,
+                   "tile_mask_p": w.block_mask_p, "dropout": w.rho, "allowed_pairs": pairs},
+        "frac_peak": value / peak,
+        "fwd": {"ms": kern_ms["fwd"], "TFLOP/s": fwd_tf, "frac_peak": fwd_tf / peak},
+        "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_tf, "frac_peak": bwd_tf / peak},
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_dense(w, arr, block_mask)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_causal_bf16_b4h16_n2048_d128", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the (batch, head) lanes shard with no exchange, so N GPUs would each run this "
+              "same per-GPU workload)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.WORKLOADS[args.workload]
+    if isinstance(w, workloads.DenseWorkload):
+        out = bench_dense(w, args)
+    else:
+        print(f"{w.name}: the sparse path is not benchmarked by this build", file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

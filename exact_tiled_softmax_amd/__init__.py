@@ -6,7 +6,7 @@ through ctypes.  Pointer arguments accept an integer device address, None, or
 any object with ``data_ptr()`` (a torch tensor).  ``stream`` defaults to the
 current torch stream when torch is importable, else the default stream.
 
-The library must be built (``python -m exact_tiled_softmax_amd.build``);
+The library must be built (``python exact_tiled_softmax_amd/build.py``);
 importing this package raises if libattn.so is missing.  There is no fallback
 implementation.
 """
@@ -17,7 +17,7 @@ import os
 __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "AttnError", "Mask", "Dropout",
-    "attn_fwd", "attn_bwd", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
+    "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_status_string", "library_path", "lib",
 ]
 
@@ -29,7 +29,7 @@ library_path = os.path.join(_HERE, "libattn.so")
 
 if not os.path.exists(library_path):
     raise ImportError(
-        f"{library_path} is missing: build it with `python -m exact_tiled_softmax_amd.build` "
+        f"{library_path} is missing: build it with `python exact_tiled_softmax_amd/build.py` "
         "(there is no fallback implementation)")
 
 lib = ctypes.CDLL(library_path)
@@ -58,6 +58,8 @@ lib.attn_bwd_workspace_size.restype = _sz
 lib.attn_bwd_workspace_size.argtypes = [_i] * 8
 lib.attn_bwd.restype = _i
 lib.attn_bwd.argtypes = ([_i] + [_i] * 7 + [_vp] * 6 + [_pm, _f, _i, _pd] + [_vp] * 3 + [_vp, _sz, _vp])
+lib.attn_bwd_phase.restype = _i
+lib.attn_bwd_phase.argtypes = [_i] + lib.attn_bwd.argtypes
 lib.attn_sparse_fwd.restype = _i
 lib.attn_sparse_fwd.argtypes = [_i] + [_i] * 6 + [_vp] * 5 + [_f, _vp, _vp, _vp]
 lib.attn_sparse_bwd_workspace_size.restype = _sz
@@ -140,6 +142,15 @@ def attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, b
                       _ptr(G), _mask(mask), float(scale), int(block_b), _drop(dropout), _ptr(dQ),
                       _ptr(dK), _ptr(dV), _ptr(workspace), int(workspace_bytes), _stream(stream))
     return _check(st, "attn_bwd", raise_on_error)
+
+
+def attn_bwd_phase(phases, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b,
+                   dropout, dQ, dK, dV, workspace, workspace_bytes, stream=None, raise_on_error=True):
+    st = lib.attn_bwd_phase(int(phases), dt, B, H, H_kv, n_q, n_k, d, dv, _ptr(Q), _ptr(K), _ptr(V), _ptr(Y),
+                            _ptr(LSE), _ptr(G), _mask(mask), float(scale), int(block_b), _drop(dropout),
+                            _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace), int(workspace_bytes),
+                            _stream(stream))
+    return _check(st, "attn_bwd_phase", raise_on_error)
 
 
 def attn_sparse_fwd(dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,

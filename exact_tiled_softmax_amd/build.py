@@ -1,6 +1,6 @@
 """Build libattn.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: python -m exact_tiled_softmax_amd.build [-v]
+Usage: python exact_tiled_softmax_amd/build.py [-v]   (runs without importing the package)
 
 Each source is compiled to an object under <repo>/_build/ (in parallel), then
 linked into exact_tiled_softmax_amd/libattn.so next to this file.  Packed fp32

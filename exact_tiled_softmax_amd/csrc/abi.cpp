@@ -121,27 +121,50 @@ size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, i
   return round_up((size_t)B * H * n_q * sizeof(float));
 }
 
-attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
-                     const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
-                     const void* G, const attn_mask_t* mask, float scale, int block_b,
-                     const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
+                              int dv, const void* Q, const void* K, const void* V, const void* Y,
+                              const float* LSE, const void* G, const attn_mask_t* mask, float scale,
+                              int block_b, const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_dense(dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
   if (st != ATTN_OK) return st;
-  if (!Q || !K || !V || !Y || !LSE || !G || !dQ || !dK || !dV) return ATTN_ERR_INVALID_ARG;
+  if (phases < 1 || phases > 7) return ATTN_ERR_INVALID_ARG;
   const size_t al = dt == ATTN_F32 ? 4 : 16;
+  // pointers each phase reads or writes
+  const bool p0 = phases & 1, p1 = phases & 2, p2 = phases & 4;
+  if ((p0 && (!Y || !G)) || ((p1 || p2) && (!Q || !K || !V || !LSE || !G)) || (p1 && (!dK || !dV)) ||
+      (p2 && !dQ))
+    return ATTN_ERR_INVALID_ARG;
   for (const void* p : {Q, K, V, Y, G, (const void*)dQ, (const void*)dK, (const void*)dV})
-    if (!aligned(p, al)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(LSE, 4)) return ATTN_ERR_INVALID_ARG;
+    if (p && !aligned(p, al)) return ATTN_ERR_INVALID_ARG;
+  if (LSE && !aligned(LSE, 4)) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
   DenseArgs a;
   fill_dense(a, dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
   a.Q = Q; a.K = K; a.V = V; a.Y = Y; a.LSE = (float*)LSE; a.G = G;
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.Dws = (float*)workspace;
-  const int rc = dt == ATTN_F32 ? launch_dense_bwd_f32(a, stream)
-                                : launch_dense_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
+  const int rc = dt == ATTN_F32 ? launch_dense_bwd_f32(a, stream, phases)
+                                : launch_dense_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream, phases);
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                     const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
+                     const void* G, const attn_mask_t* mask, float scale, int block_b,
+                     const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(7, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout,
+                    dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
+                           int dv, const void* Q, const void* K, const void* V, const void* Y,
+                           const float* LSE, const void* G, const attn_mask_t* mask, float scale,
+                           int block_b, const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(phases, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b,
+                    dropout, dQ, dK, dV, workspace, workspace_bytes, stream);
 }
 
 static attn_status check_sparse(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,

@@ -88,7 +88,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
   const int nq = a.nq, nk = a.nk;
-  const int kb = blockIdx.x, bg = blockIdx.y;  // key block, (batch, kv head)
+  const int BG = a.B * a.Hkv;
+  const int kb = (int)(blockIdx.x / BG), bg = (int)(blockIdx.x % BG);  // key block, (batch, kv head)
   const int b = bg / a.Hkv, g = bg % a.Hkv, grp = a.H / a.Hkv;
   const int k0 = kb * 128, kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
@@ -470,27 +471,31 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
 }
 
 template <class E, int D>
-static int launch_bwd_t(const DenseArgs& a, void* stream) {
+static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
   hipStream_t st = (hipStream_t)stream;
-  const int rows = a.B * a.H * a.nq;
-  const int prep_threads = rows * (D / 8);
-  hipLaunchKernelGGL((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows);
-  dim3 gk((a.nk + 127) / 128, a.B * a.Hkv);
+  if (phases & 1) {
+    const int rows = a.B * a.H * a.nq;
+    const int prep_threads = rows * (D / 8);
+    hipLaunchKernelGGL((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows);
+  }
+  const int n_kblocks = (a.nk + 127) / 128;
+  dim3 gk(n_kblocks * a.B * a.Hkv);
   const int n_qtiles = (a.nq + 127) / 128;
   dim3 gq(n_qtiles * a.B * a.H);
   if (a.drop.enabled) {
-    hipLaunchKernelGGL((dense_bwd_dkdv_kernel<E, D, true>), gk, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((dense_bwd_dq_kernel<E, D, true>), gq, dim3(256), 0, st, a, n_qtiles);
+    if (phases & 2) hipLaunchKernelGGL((dense_bwd_dkdv_kernel<E, D, true>), gk, dim3(256), 0, st, a);
+    if (phases & 4) hipLaunchKernelGGL((dense_bwd_dq_kernel<E, D, true>), gq, dim3(256), 0, st, a, n_qtiles);
   } else {
-    hipLaunchKernelGGL((dense_bwd_dkdv_kernel<E, D, false>), gk, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((dense_bwd_dq_kernel<E, D, false>), gq, dim3(256), 0, st, a, n_qtiles);
+    if (phases & 2) hipLaunchKernelGGL((dense_bwd_dkdv_kernel<E, D, false>), gk, dim3(256), 0, st, a);
+    if (phases & 4) hipLaunchKernelGGL((dense_bwd_dq_kernel<E, D, false>), gq, dim3(256), 0, st, a, n_qtiles);
   }
   return (int)hipGetLastError();
 }
 
-int launch_dense_bwd(const DenseArgs& a, Dt dt, void* stream) {
-  if (dt == Dt::BF16) return a.d == 128 ? launch_bwd_t<BF16, 128>(a, stream) : launch_bwd_t<BF16, 64>(a, stream);
-  return a.d == 128 ? launch_bwd_t<F16, 128>(a, stream) : launch_bwd_t<F16, 64>(a, stream);
+int launch_dense_bwd(const DenseArgs& a, Dt dt, void* stream, int phases) {
+  if (dt == Dt::BF16)
+    return a.d == 128 ? launch_bwd_t<BF16, 128>(a, stream, phases) : launch_bwd_t<BF16, 64>(a, stream, phases);
+  return a.d == 128 ? launch_bwd_t<F16, 128>(a, stream, phases) : launch_bwd_t<F16, 64>(a, stream, phases);
 }
 
 }  // namespace ets

@@ -193,17 +193,17 @@ int launch_dense_fwd_f32(const DenseArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_dense_bwd_f32(const DenseArgs& a, void* stream) {
+int launch_dense_bwd_f32(const DenseArgs& a, void* stream, int phases) {
   hipStream_t st = (hipStream_t)stream;
   const int rows = a.B * a.H * a.nq;
-  hipLaunchKernelGGL(f32_prep_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, a, rows);
+  if (phases & 1) hipLaunchKernelGGL(f32_prep_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, a, rows);
   dim3 gq((a.nq + 63) / 64, a.B * a.H), gk((a.nk + 63) / 64, a.B * a.Hkv);
   if (a.d <= 32 && a.dv <= 32) {
-    hipLaunchKernelGGL(f32_dq_kernel<32>, gq, dim3(64), 0, st, a);
-    hipLaunchKernelGGL(f32_dkdv_kernel<32>, gk, dim3(64), 0, st, a);
+    if (phases & 2) hipLaunchKernelGGL(f32_dkdv_kernel<32>, gk, dim3(64), 0, st, a);
+    if (phases & 4) hipLaunchKernelGGL(f32_dq_kernel<32>, gq, dim3(64), 0, st, a);
   } else {
-    hipLaunchKernelGGL(f32_dq_kernel<128>, gq, dim3(64), 0, st, a);
-    hipLaunchKernelGGL(f32_dkdv_kernel<128>, gk, dim3(64), 0, st, a);
+    if (phases & 2) hipLaunchKernelGGL(f32_dkdv_kernel<128>, gk, dim3(64), 0, st, a);
+    if (phases & 4) hipLaunchKernelGGL(f32_dq_kernel<128>, gq, dim3(64), 0, st, a);
   }
   return (int)hipGetLastError();
 }

@@ -57,9 +57,10 @@ struct SparseArgs {
 // Kernel launchers (defined in the .hip files).  Each returns 0 on success or
 // a hipError_t value.  They assume validated arguments.
 int launch_dense_fwd(const DenseArgs& a, Dt dt, void* stream);
-int launch_dense_bwd(const DenseArgs& a, Dt dt, void* stream);
+// phases: bit 0 = D prepass, bit 1 = dK/dV, bit 2 = dQ
+int launch_dense_bwd(const DenseArgs& a, Dt dt, void* stream, int phases);
 int launch_dense_fwd_f32(const DenseArgs& a, void* stream);
-int launch_dense_bwd_f32(const DenseArgs& a, void* stream);
+int launch_dense_bwd_f32(const DenseArgs& a, void* stream, int phases);
 int launch_sparse_fwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_sparse_bwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_dropout_mask(const DropArgs& d, int B, int H, int nq, int nk, uint8_t* xi, void* stream);

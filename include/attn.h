@@ -143,6 +143,25 @@ attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, in
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_phase -- the three launches of attn_bwd, selectable, for callers
+ * that schedule them themselves (for instance the dK/dV and dQ phases on two
+ * streams once the prepass is done) or time them one by one.  `phases` is a
+ * bit set: 1 = the prepass D_i = G_i . Y_i into the workspace, 2 = dK and dV,
+ * 4 = dQ; phases 2 and 4 read the D_i a completed phase 1 left in the same
+ * workspace and are independent of each other.  attn_bwd is phases = 7.
+ * Pointers a selected phase does not use may be NULL (phase 1 reads Y and G;
+ * phases 2 and 4 read Q, K, V, LSE and G; phase 2 writes dK, dV; phase 4
+ * writes dQ).  Other arguments and errors as attn_bwd; phases outside 1..7
+ * is ATTN_ERR_INVALID_ARG.
+ */
+attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k,
+                           int d, int dv, const void* Q, const void* K, const void* V,
+                           const void* Y, const float* LSE, const void* G,
+                           const attn_mask_t* mask, float scale, int block_b,
+                           const attn_dropout_t* dropout, void* dQ, void* dK, void* dV,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_sparse_fwd -- shared-KV top-k sparse attention with sink ([P5]
  * sections 1, 2 and 7.1).  For token t and head h, with the selected rows
  * I = topk_idx[t][0 : L_t] (L_t = topk_length[t], or topk when NULL):
