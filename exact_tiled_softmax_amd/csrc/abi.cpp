@@ -208,7 +208,7 @@ attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
 size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk) {
   (void)d_v; (void)topk;
   if (bad_dims({Tq, H, Tkv, d_qk})) return 0;
-  return round_up((size_t)Tq * H * sizeof(float)) + round_up((size_t)Tkv * d_qk * sizeof(float));
+  return 2 * round_up((size_t)Tq * H * sizeof(float)) + round_up((size_t)Tkv * d_qk * sizeof(float));
 }
 
 attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
@@ -232,7 +232,8 @@ attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
   a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
   a.O = (void*)O; a.LSE = (float*)LSE; a.dO = dO; a.dQ = dQ; a.dKV = dKV; a.dSink = dSink;
   a.Dws = (float*)workspace;
-  a.dKVws = (float*)((char*)workspace + round_up((size_t)Tq * H * sizeof(float)));
+  a.dsink_part = (float*)((char*)workspace + round_up((size_t)Tq * H * sizeof(float)));
+  a.dKVws = (float*)((char*)workspace + 2 * round_up((size_t)Tq * H * sizeof(float)));
   const int rc = launch_sparse_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -62,10 +62,11 @@ __device__ __forceinline__ unsigned keep4_rows(const DropArgs& d, int lane_bh, i
 }
 
 // Allowed bits of query rows i0..i0+3 (bit r <-> row i0 + r) for key j.
-__device__ __forceinline__ unsigned allowed4_rows(const MaskArgs& m, int i0, int j, int nq, int nk) {
+__device__ __forceinline__ unsigned allowed4_rows(const MaskArgs& m, int i0, int j, int nq, int nk,
+                                                  bool check_bm) {
   unsigned bits = 0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) bits |= (allowed4(m, i0 + r, j, nq, nk) & 1u) << r;
+  for (int r = 0; r < 4; ++r) bits |= (allowed1(m, i0 + r, j, nq, nk, check_bm) ? 1u : 0u) << r;
   return bits;
 }
 
@@ -197,7 +198,9 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     const char ETS_LDS* gt_ = qt_ + TILEB;
     const float ETS_LDS* ls = (const float ETS_LDS*)(gt_ + TILEB);
     const float ETS_LDS* ds = ls + BQ;
-    const int cls = classify(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nq, nk);
+    const int cinfo = classify(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nq, nk);
+    const int cls = cinfo & kClassMask;
+    const bool cbm = (cinfo & kCheckBlockMask) != 0;
 
     if (cls != kEmpty) {
       vec8 pb[4], gb[4];  // P~ and gamma as B operands, k-steps of 16 queries
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
           const f32x4 d4 = *(const f32x4 ETS_LDS*)(ds + qr);
           const float lv[4] = {l4[0], l4[1], l4[2], l4[3]}, dvv[4] = {d4[0], d4[1], d4[2], d4[3]};
           unsigned allow = 0xFu, keep = 0xFu;
-          if (cls == kPartial) allow = allowed4_rows(a.mask, qb0 + qr, key, nq, nk);
+          if (cls == kPartial) allow = allowed4_rows(a.mask, qb0 + qr, key, nq, nk, cbm);
           if constexpr (DROP) keep = keep4_rows(a.drop, lane_bh, qb0 + qr, key);
           float p[4], pk[4], gm[4];
 #pragma unroll
@@ -395,7 +398,9 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
     const char ETS_LDS* kt = smem + stage * 2 * TILEB;
     const char ETS_LDS* vt = kt + TILEB;
     const int j0 = jt * BK;
-    const int cls = classify(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
+    const int cinfo = classify(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
+    const int cls = cinfo & kClassMask;
+    const bool cbm = (cinfo & kCheckBlockMask) != 0;
 
     if (cls != kEmpty) {
       f32x16 sc[2], dp[2];
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
         for (int g4 = 0; g4 < 4; ++g4) {
           const int jj = j0 + 32 * mb + 8 * g4 + 4 * h32;
           unsigned allow = 0xFu, keep = 0xFu;
-          if (cls == kPartial) allow = allowed4(a.mask, q, jj, nq, nk);
+          if (cls == kPartial) allow = allowed4(a.mask, q, jj, nq, nk, cbm);
           if constexpr (DROP) keep = keep4(a.drop, bh, q, jj);
           float gm[4];
 #pragma unroll
@@ -476,20 +481,20 @@ static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
   if (phases & 1) {
     const int rows = a.B * a.H * a.nq;
     const int prep_threads = rows * (D / 8);
-    hipLaunchKernelGGL((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows);
+    ETS_TRY(launch((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows));
   }
   const int n_kblocks = (a.nk + 127) / 128;
   dim3 gk(n_kblocks * a.B * a.Hkv);
   const int n_qtiles = (a.nq + 127) / 128;
   dim3 gq(n_qtiles * a.B * a.H);
   if (a.drop.enabled) {
-    if (phases & 2) hipLaunchKernelGGL((dense_bwd_dkdv_kernel<E, D, true>), gk, dim3(256), 0, st, a);
-    if (phases & 4) hipLaunchKernelGGL((dense_bwd_dq_kernel<E, D, true>), gq, dim3(256), 0, st, a, n_qtiles);
+    if (phases & 2) ETS_TRY(launch((dense_bwd_dkdv_kernel<E, D, true>), gk, dim3(256), 0, st, a));
+    if (phases & 4) ETS_TRY(launch((dense_bwd_dq_kernel<E, D, true>), gq, dim3(256), 0, st, a, n_qtiles));
   } else {
-    if (phases & 2) hipLaunchKernelGGL((dense_bwd_dkdv_kernel<E, D, false>), gk, dim3(256), 0, st, a);
-    if (phases & 4) hipLaunchKernelGGL((dense_bwd_dq_kernel<E, D, false>), gq, dim3(256), 0, st, a, n_qtiles);
+    if (phases & 2) ETS_TRY(launch((dense_bwd_dkdv_kernel<E, D, false>), gk, dim3(256), 0, st, a));
+    if (phases & 4) ETS_TRY(launch((dense_bwd_dq_kernel<E, D, false>), gq, dim3(256), 0, st, a, n_qtiles));
   }
-  return (int)hipGetLastError();
+  return 0;
 }
 
 int launch_dense_bwd(const DenseArgs& a, Dt dt, void* stream, int phases) {

@@ -17,10 +17,6 @@
 
 namespace ets {
 
-__device__ __forceinline__ bool allowed1(const MaskArgs& m, int i, int j, int nq, int nk) {
-  return (allowed4(m, i, j, nq, nk) & 1u) != 0u;
-}
-
 __device__ __forceinline__ float kappa1(const DropArgs& d, int lane_bh, int i, int j) {
   if (!d.enabled) return 1.f;
   return ((keep4(d, lane_bh, i, j & ~3) >> (j & 3)) & 1u) ? d.inv_keep : 0.f;
@@ -187,25 +183,25 @@ int launch_dense_fwd_f32(const DenseArgs& a, void* stream) {
   dim3 grid((a.nq + 63) / 64, a.B * a.H), block(64);
   hipStream_t st = (hipStream_t)stream;
   if (a.d <= 32 && a.dv <= 32)
-    hipLaunchKernelGGL(f32_fwd_kernel<32>, grid, block, 0, st, a);
+    ETS_TRY(launch(f32_fwd_kernel<32>, grid, block, 0, st, a));
   else
-    hipLaunchKernelGGL(f32_fwd_kernel<128>, grid, block, 0, st, a);
-  return (int)hipGetLastError();
+    ETS_TRY(launch(f32_fwd_kernel<128>, grid, block, 0, st, a));
+  return 0;
 }
 
 int launch_dense_bwd_f32(const DenseArgs& a, void* stream, int phases) {
   hipStream_t st = (hipStream_t)stream;
   const int rows = a.B * a.H * a.nq;
-  if (phases & 1) hipLaunchKernelGGL(f32_prep_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, a, rows);
+  if (phases & 1) ETS_TRY(launch(f32_prep_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, a, rows));
   dim3 gq((a.nq + 63) / 64, a.B * a.H), gk((a.nk + 63) / 64, a.B * a.Hkv);
   if (a.d <= 32 && a.dv <= 32) {
-    if (phases & 2) hipLaunchKernelGGL(f32_dkdv_kernel<32>, gk, dim3(64), 0, st, a);
-    if (phases & 4) hipLaunchKernelGGL(f32_dq_kernel<32>, gq, dim3(64), 0, st, a);
+    if (phases & 2) ETS_TRY(launch(f32_dkdv_kernel<32>, gk, dim3(64), 0, st, a));
+    if (phases & 4) ETS_TRY(launch(f32_dq_kernel<32>, gq, dim3(64), 0, st, a));
   } else {
-    if (phases & 2) hipLaunchKernelGGL(f32_dkdv_kernel<128>, gk, dim3(64), 0, st, a);
-    if (phases & 4) hipLaunchKernelGGL(f32_dq_kernel<128>, gq, dim3(64), 0, st, a);
+    if (phases & 2) ETS_TRY(launch(f32_dkdv_kernel<128>, gk, dim3(64), 0, st, a));
+    if (phases & 4) ETS_TRY(launch(f32_dq_kernel<128>, gq, dim3(64), 0, st, a));
   }
-  return (int)hipGetLastError();
+  return 0;
 }
 
 }  // namespace ets

@@ -30,7 +30,7 @@ namespace ets {
 constexpr float kRescaleSlack = 8.0f;
 
 template <class E, int D, int NB, bool DROP>
-__global__ __launch_bounds__(256, 1) void dense_fwd_kernel(const DenseArgs a, int n_qtiles) {
+__global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const DenseArgs a, int n_qtiles) {
   constexpr int BK = 64;
   constexpr int NQW = 32 * NB;
   constexpr int BQ = 4 * NQW;
@@ -142,7 +142,9 @@ __global__ __launch_bounds__(256, 1) void dense_fwd_kernel(const DenseArgs a, in
     const char ETS_LDS* kt = smem + stage * 2 * TILEB;
     const char ETS_LDS* vt = kt + TILEB;
     const int j0 = jt * BK;
-    const int cls = classify(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
+    const int cinfo = classify(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
+    const int cls = cinfo & kClassMask;
+    const bool cbm = (cinfo & kCheckBlockMask) != 0;
 
     if (cls != kEmpty) {
       // ---- S^T = K Q^T: rows are keys j0 + 32mb + (8(r/4) + 4h32 + r%4)
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, 1) void dense_fwd_kernel(const DenseArgs a, in
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              allow[mb][g4] = allowed4(a.mask, qi, j0 + 32 * mb + 8 * g4 + 4 * h32, nq, nk);
+              allow[mb][g4] = allowed4(a.mask, qi, j0 + 32 * mb + 8 * g4 + 4 * h32, nq, nk, cbm);
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 if (!((allow[mb][g4] >> r) & 1u)) s[mb][nb][4 * g4 + r] = kNegInf;
@@ -284,21 +286,21 @@ static int launch_fwd_t(const DenseArgs& a, void* stream) {
   const int n_qtiles = (a.nq + BQ - 1) / BQ;
   dim3 grid(n_qtiles * a.B * a.H), block(256);
   if (a.drop.enabled)
-    hipLaunchKernelGGL((dense_fwd_kernel<E, D, NB, true>), grid, block, 0, (hipStream_t)stream, a, n_qtiles);
+    ETS_TRY(launch((dense_fwd_kernel<E, D, NB, true>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
   else
-    hipLaunchKernelGGL((dense_fwd_kernel<E, D, NB, false>), grid, block, 0, (hipStream_t)stream, a, n_qtiles);
-  return (int)hipGetLastError();
+    ETS_TRY(launch((dense_fwd_kernel<E, D, NB, false>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
+  return 0;
 }
 
 bool dense_mfma_supported(int d, int dv) { return d == dv && (d == 64 || d == 128); }
 
 int launch_dense_fwd(const DenseArgs& a, Dt dt, void* stream) {
   if (dt == Dt::BF16) {
-    if (a.d == 128) return launch_fwd_t<BF16, 128, 2>(a, stream);
-    return launch_fwd_t<BF16, 64, 2>(a, stream);
+    if (a.d == 128) return launch_fwd_t<BF16, 128, 1>(a, stream);
+    return launch_fwd_t<BF16, 64, 1>(a, stream);
   }
-  if (a.d == 128) return launch_fwd_t<F16, 128, 2>(a, stream);
-  return launch_fwd_t<F16, 64, 2>(a, stream);
+  if (a.d == 128) return launch_fwd_t<F16, 128, 1>(a, stream);
+  return launch_fwd_t<F16, 64, 1>(a, stream);
 }
 
 }  // namespace ets

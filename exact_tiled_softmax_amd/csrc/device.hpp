@@ -4,6 +4,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <tuple>
 
 #include "params.hpp"
 
@@ -22,6 +23,26 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define ETS_LDS __attribute__((address_space(3)))
+
+// Launch with the status of this launch only (hipGetLastError would also
+// report errors left behind by unrelated earlier runtime calls).
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> vals(args...);
+  void* ptrs[sizeof...(P)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&v), ...);
+  }, vals);
+  return hipLaunchKernel((const void*)kernel, grid, block, ptrs, lds, st);
+}
+
+#define ETS_TRY(expr)                      \
+  do {                                     \
+    const hipError_t ets_e_ = (expr);      \
+    if (ets_e_ != hipSuccess) return (int)ets_e_; \
+  } while (0)
 
 // ------------------------------------------------------------ element types
 // Storage is 16-bit in memory; MFMA operands are 8 elements (16 bytes) per lane.
@@ -164,7 +185,10 @@ __device__ __forceinline__ unsigned keep4(const DropArgs& d, int lane_bh, int i,
 
 // ------------------------------------------------------------ allowed sets
 // Allowed bits of keys j0 .. j0+3 for query row i (bit r <-> key j0 + r).
-__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk) {
+// check_bm = false skips the block-mask lookup (the caller has established
+// that the block mask allows the whole tile).
+__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk,
+                                             bool check_bm = true) {
   if (i >= nq) return 0u;
   unsigned bits = 0;
 #pragma unroll
@@ -173,17 +197,29 @@ __device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, i
     bool ok = j < nk;
     if (m.causal) ok = ok && (j <= i);
     if (m.window > 0) ok = ok && (i - j < m.window);
-    if (ok && m.block_mask) ok = m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] != 0;
+    if (check_bm && ok && m.block_mask) ok = m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] != 0;
     if (ok && m.dense_mask) ok = m.dense_mask[(size_t)i * nk + j] != 0;
     bits |= (unsigned)ok << r;
   }
   return bits;
 }
 
-enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2 };
+// Single (row i, key j) test.
+__device__ __forceinline__ bool allowed1(const MaskArgs& m, int i, int j, int nq, int nk, bool check_bm = true) {
+  if (i >= nq || j >= nk) return false;
+  if (m.causal && j > i) return false;
+  if (m.window > 0 && i - j >= m.window) return false;
+  if (check_bm && m.block_mask && m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] == 0) return false;
+  if (m.dense_mask && m.dense_mask[(size_t)i * nk + j] == 0) return false;
+  return true;
+}
+
+enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2, kClassMask = 3, kCheckBlockMask = 4 };
 
 // Classify the rectangle of query rows [ia, ib] x keys [ja, jb] (inclusive;
 // jb may run past nk for a ragged last tile).  Uniform across the wave.
+// Returns kEmpty, kFull or kPartial, plus kCheckBlockMask when the block mask
+// is mixed inside the rectangle and must be read per element.
 __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int ja, int jb, int nq, int nk) {
   if (ia >= nq || ja >= nk) return kEmpty;
   if (ib >= nq) ib = nq - 1;
@@ -200,7 +236,7 @@ __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int j
   if (m.block_mask) {
     const int r0 = ia / m.bq, r1 = ib / m.bq, c0 = ja / m.bk, c1 = jb / m.bk;
     if ((r1 - r0 + 1) * (c1 - c0 + 1) > 64) {
-      cls = kPartial;
+      cls = kPartial | kCheckBlockMask;
     } else {
       int ones = 0, tot = 0;
       for (int r = r0; r <= r1; ++r)
@@ -209,10 +245,10 @@ __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int j
           ++tot;
         }
       if (ones == 0) return kEmpty;
-      if (ones != tot) cls = kPartial;
+      if (ones != tot) cls = kPartial | kCheckBlockMask;
     }
   }
-  if (m.dense_mask) cls = kPartial;
+  if (m.dense_mask) cls = (cls & kCheckBlockMask) | kPartial;
   return cls;
 }
 

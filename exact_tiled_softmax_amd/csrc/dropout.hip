@@ -24,9 +24,9 @@ __global__ __launch_bounds__(256) void dropout_mask_kernel(const DropArgs d, int
 int launch_dropout_mask(const DropArgs& d, int B, int H, int nq, int nk, uint8_t* xi, void* stream) {
   const long long groups = (long long)B * H * nq * ((nk + 3) / 4);
   const long long blocks = (groups + 255) / 256;
-  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
-                     (hipStream_t)stream, d, H, nq, nk, groups, xi);
-  return (int)hipGetLastError();
+  ETS_TRY(launch(dropout_mask_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
+                     (hipStream_t)stream, d, H, nq, nk, groups, xi));
+  return 0;
 }
 
 }  // namespace ets

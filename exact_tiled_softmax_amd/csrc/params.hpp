@@ -48,7 +48,8 @@ struct SparseArgs {
   void* O; float* LSE;
   const void* dO;
   void* dQ; void* dKV; float* dSink;
-  float* Dws;        // [Tq*H]
+  float* Dws;        // [Tq*H]  D = dO . O
+  float* dsink_part; // [Tq*H]  -p_sink D per (token, head)
   float* dKVws;      // [Tkv*dqk] fp32 accumulation
   int Tq, H, Tkv, dqk, dv, topk;
   float scale, scale_log2;

@@ -186,8 +186,8 @@ attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
                             const int32_t* topk_length, const float* attn_sink, float scale,
                             void* O, float* LSE, void* stream);
 
-/* Bytes of device workspace attn_sparse_bwd needs (fp32 D per (token, head)
- * and an fp32 [Tkv][d_qk] dKV accumulator). */
+/* Bytes of device workspace attn_sparse_bwd needs (fp32 D and sink-gradient
+ * terms per (token, head), and an fp32 [Tkv][d_qk] dKV accumulator). */
 size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk);
 
 /*
@@ -198,8 +198,10 @@ size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v,
  * dSink[h] = -sum_t p_sink(t, h) D(t, h).
  * Arguments as attn_sparse_fwd, plus O and LSE as attn_sparse_fwd wrote them,
  * dO [Tq][H][d_v], outputs dQ [Tq][H][d_qk], dKV [Tkv][d_qk] and dSink fp32 [H]
- * (required iff attn_sink is not NULL), and the workspace.  dKV is summed with
- * fp32 atomics, so its bits may differ between runs.
+ * (required iff attn_sink is not NULL), and the workspace (256-byte aligned,
+ * at least attn_sparse_bwd_workspace_size() bytes; contents on entry are
+ * ignored).  dKV is summed with fp32 atomics, so its bits may differ between
+ * runs; dSink is summed over tokens in a fixed order.
  */
 attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
                             const void* Q, const void* KV, const int32_t* topk_idx,

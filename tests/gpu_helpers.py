@@ -94,3 +94,39 @@ def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=
     res = {k: (from_dev(v, dtype) if k != "LSE" else v.cpu().numpy().astype(np.float64)) for k, v in out.items()}
     res["_dev"] = out
     return res
+
+
+def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None):
+    """Run attn_sparse_fwd (and attn_sparse_bwd when dO is given)."""
+    import exact_tiled_softmax_amd as ets
+    torch = torch_cuda()
+    Tq, H, dqk = Q.shape
+    Tkv = KV.shape[0]
+    dv = 512 if dO is None else dO.shape[2]
+    topk = idx.shape[1]
+    dt = DT[dtype]
+    q, kv = to_dev(Q, dtype), to_dev(KV, dtype)
+    di = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+    dl = None if length is None else torch.from_numpy(np.ascontiguousarray(length, np.int32)).cuda()
+    ds = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, np.float32)).cuda()
+    O = empty((Tq, H, dv), dtype)
+    LSE = torch.zeros((Tq, H), dtype=torch.float32, device="cuda")
+    ets.attn_sparse_fwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE)
+    out = {"O": O, "LSE": LSE}
+    if dO is not None:
+        g = to_dev(dO, dtype)
+        dQ, dKV = empty(Q.shape, dtype), empty(KV.shape, dtype)
+        dSink = torch.zeros(H, dtype=torch.float32, device="cuda") if sink is not None else None
+        nb = ets.attn_sparse_bwd_workspace_size(Tq, H, Tkv, dqk, dv, topk)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        ets.attn_sparse_bwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE, g, dQ, dKV, dSink,
+                            ws, nb)
+        out.update(dQ=dQ, dKV=dKV)
+        if dSink is not None:
+            out["dSink"] = dSink
+    torch.cuda.synchronize()
+    res = {}
+    for k, v in out.items():
+        res[k] = v.cpu().numpy().astype(np.float64) if k in ("LSE", "dSink") else from_dev(v, dtype)
+    res["_dev"] = out
+    return res

@@ -46,7 +46,7 @@ def test_workspace_sizes():
     import exact_tiled_softmax_amd as ets
     assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 4, 16, 16, 2048, 2048, 128, 128) == 4 * 16 * 2048 * 4
     assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 0, 16, 16, 2048, 2048, 128, 128) == 0
-    assert ets.attn_sparse_bwd_workspace_size(4096, 64, 16384, 576, 512, 2048) == 4096 * 64 * 4 + 16384 * 576 * 4
+    assert ets.attn_sparse_bwd_workspace_size(4096, 64, 16384, 576, 512, 2048) == 2 * 4096 * 64 * 4 + 16384 * 576 * 4
 
 
 P = 0x10000  # a dummy aligned address: never dereferenced, every call fails validation
@@ -86,7 +86,6 @@ def test_bwd_rejects_small_workspace_before_launch():
     dict(dt=0, code=2), dict(H=32, code=2), dict(d_qk=512, code=2), dict(Tq=0, code=1),
     dict(d_v=600, code=1), dict(scale=-1.0, code=1), dict(idx=None, code=1), dict(KV=P + 4, code=1),
 ])
-@pytest.mark.skip(reason="sparse kernels are not in this build yet")
 def test_sparse_fwd_rejects_before_launch(case):
     import exact_tiled_softmax_amd as ets
     a = dict(dt=ets.ATTN_BF16, Tq=8, H=64, Tkv=32, d_qk=576, d_v=512, topk=16, KV=P, idx=P, scale=0.04)
@@ -96,7 +95,6 @@ def test_sparse_fwd_rejects_before_launch(case):
     assert st == case["code"]
 
 
-@pytest.mark.skip(reason="sparse kernels are not in this build yet")
 def test_sparse_bwd_needs_dsink_with_sink_and_a_workspace():
     import exact_tiled_softmax_amd as ets
     need = ets.attn_sparse_bwd_workspace_size(8, 64, 32, 576, 512, 16)
