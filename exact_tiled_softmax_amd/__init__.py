@@ -32,6 +32,30 @@ if not os.path.exists(library_path):
         f"{library_path} is missing: build it with `python exact_tiled_softmax_amd/build.py` "
         "(there is no fallback implementation)")
 
+
+
+def _share_torch_hip_runtime():
+    """Make libattn.so bind to the HIP runtime PyTorch uses.
+
+    The PyTorch wheel ships its own libamdhip64.so.  If libattn.so were loaded
+    first it would pull in the system runtime, and a later `import torch` would
+    add a second runtime to the process: device memory and streams from one,
+    launches on the other.  Loading PyTorch's copy first (same SONAME) makes the
+    dynamic linker resolve libattn.so against it.  Without PyTorch the system
+    runtime is used."""
+    import importlib.util
+    import sys
+    if "torch" in sys.modules:
+        return
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        return
+    path = os.path.join(os.path.dirname(spec.origin), "lib", "libamdhip64.so")
+    if os.path.exists(path):
+        ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+
+
+_share_torch_hip_runtime()
 lib = ctypes.CDLL(library_path)
 
 

@@ -110,3 +110,12 @@ def test_dropout_mask_rejects_bad_rate():
     import exact_tiled_softmax_amd as ets
     assert ets.attn_dropout_mask(1.0, 0, 1, 1, 4, 4, P, stream=0, raise_on_error=False) == ets.ATTN_ERR_INVALID_ARG
     assert ets.attn_dropout_mask(0.1, 0, 1, 1, 4, 4, None, stream=0, raise_on_error=False) == ets.ATTN_ERR_INVALID_ARG
+
+
+def test_one_hip_runtime_per_process():
+    # the library binds to the HIP runtime PyTorch loads, whatever the import order
+    code = ("import exact_tiled_softmax_amd, torch\n"
+            "m = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(m))\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, check=True).stdout
+    assert out.strip().splitlines()[-1] == "1"
