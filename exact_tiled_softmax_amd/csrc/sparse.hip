@@ -450,32 +450,38 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
       }
     }
     __syncthreads();
-    // dKV^T[cols of this wave][keys] = alpha Q^T dS + dO^T P  (contraction over the 64 heads)
+    // dKV[keys][cols of this wave] = alpha dS^T Q + P^T dO  (contraction over the 64 heads);
+    // the accumulator holds 16 consecutive columns of one key per 16 lanes,
+    // so each atomic instruction updates 4 rows x 64 contiguous bytes
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {       // 16-key blocks of the tile
-      vec8 bp[2], bd[2];
+      vec8 ap[2], ad[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int off = (16 * nb + l16) * (H * 2) + (32 * ks + 8 * G) * 2;
-        bp[ks] = as_vec8<E>(*(const u32x4 ETS_LDS*)(pbuf + off));
-        bd[ks] = as_vec8<E>(*(const u32x4 ETS_LDS*)(dbuf + off));
+        ap[ks] = as_vec8<E>(*(const u32x4 ETS_LDS*)(pbuf + off));
+        ad[ks] = as_vec8<E>(*(const u32x4 ETS_LDS*)(dbuf + off));
       }
-      const int slot = u0 + 16 * nb + l16;
-      const bool valid = slot < L;
-      const int j = valid ? idx_t[slot] : 0;
+      int jrow[4];
+      bool valid[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int slot = u0 + 16 * nb + 4 * G + r;
+        valid[r] = slot < L;
+        jrow[r] = valid[r] ? idx_t[slot] : 0;
+      }
 #pragma unroll
       for (int m = 0; m < MW; ++m) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          acc = E::mfma16(qt[m][ks], bd[ks], acc);
-          if (c0w + 16 * m < DV) accv = E::mfma16(gt[m][ks], bp[ks], accv);
+          acc = E::mfma16(ad[ks], qt[m][ks], acc);
+          if (c0w + 16 * m < DV) accv = E::mfma16(ap[ks], gt[m][ks], accv);
         }
-        if (valid) {
-          float* dst = ws + (size_t)j * DQK + c0w + 16 * m + 4 * G;
+        const int col = c0w + 16 * m + l16;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) atomicAdd(dst + r, fmaf(acc[r], al, accv[r]));
-        }
+        for (int r = 0; r < 4; ++r)
+          if (valid[r]) atomicAdd(ws + (size_t)jrow[r] * DQK + col, fmaf(acc[r], al, accv[r]));
       }
     }
     if (it + 1 < ntiles) gat.stash(smem + ((it + 1) & 1) * TILEB, tid);
