@@ -118,7 +118,8 @@ size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, i
                                int dv) {
   (void)dt; (void)H_kv; (void)n_k; (void)d; (void)dv;
   if (bad_dims({B, H, n_q})) return 0;
-  return round_up((size_t)B * H * n_q * sizeof(float));
+  // D_i and LSE_i log2(e), each with 64 padding rows
+  return 2 * round_up(((size_t)B * H * n_q + 64) * sizeof(float));
 }
 
 static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
@@ -144,6 +145,7 @@ static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv,
   fill_dense(a, dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
   a.Q = Q; a.K = K; a.V = V; a.Y = Y; a.LSE = (float*)LSE; a.G = G;
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.Dws = (float*)workspace;
+  a.Lws = (float*)((char*)workspace + round_up(((size_t)B * H * n_q + 64) * sizeof(float)));
   const int rc = dt == ATTN_F32 ? launch_dense_bwd_f32(a, stream, phases)
                                 : launch_dense_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream, phases);
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;

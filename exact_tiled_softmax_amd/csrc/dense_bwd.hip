@@ -27,6 +27,9 @@
 namespace ets {
 
 // --------------------------------------------------------------------- prep
+// D_i = G_i . Y_i and the base-2 LSE, LSE_i log2(e) (+inf for a row with an
+// empty allowed set, so every recomputed weight of it is 0).  The 64 rows after
+// the last are filled with D = 0, LSE2 = +inf: tiles of 64 rows may read them.
 template <class E, int D>
 __global__ __launch_bounds__(256) void dense_bwd_prep_kernel(const DenseArgs a, int rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
@@ -42,7 +45,17 @@ __global__ __launch_bounds__(256) void dense_bwd_prep_kernel(const DenseArgs a, 
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) a.Dws[row] = acc;
+  if (part == 0 && row < rows + 64) {
+    float l2 = __builtin_huge_valf();
+    if (row < rows) {
+      const float l = a.LSE[row];
+      l2 = (l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+    } else {
+      acc = 0.f;
+    }
+    a.Dws[row] = acc;
+    a.Lws[row] = l2;
+  }
 }
 
 // Keep bits (4 query rows i0..i0+3, this lane's key j) for the key-major
@@ -78,8 +91,6 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
   constexpr int MD = D / 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BQ * ROWB;
-  constexpr int CPR = D / 8;
-  constexpr int LD = (BQ * CPR) / 256;
   constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q, G tiles + LSE2, D
   typedef typename E::vec8 vec8;
 
@@ -90,7 +101,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
   const int h32 = lane >> 5, l32 = lane & 31;
   const int nq = a.nq, nk = a.nk;
   const int BG = a.B * a.Hkv;
-  const int kb = (int)(blockIdx.x / BG), bg = (int)(blockIdx.x % BG);  // key block, (batch, kv head)
+  const int kb = (int)(blockIdx.x / BG), bg = (int)(blockIdx.x % BG);  // key block (heavy first), (batch, kv head)
   const int b = bg / a.Hkv, g = bg % a.Hkv, grp = a.H / a.Hkv;
   const int k0 = kb * 128, kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
@@ -98,6 +109,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
   const uint16_t* Kp = (const uint16_t*)a.K + (size_t)bg * nk * D;
   const uint16_t* Vp = (const uint16_t*)a.V + (size_t)bg * nk * D;
 
+  // this wave's 32 keys as B operands of S = Q K^T and dP = G V^T
   vec8 kreg[KS], vreg[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
@@ -133,65 +145,30 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
       if (wg_nonempty(s)) return s;
     return -1;
   };
-
-  u32x4 qpre[LD], gpre[LD];
-  f32x4 lpre, dpre;
-  auto fetch = [&](int s) {
+  // Q and G tiles straight to LDS; LSE2 and D (64 floats each) by one
+  // half-wave instruction (the workspace holds 64 padding rows after the last)
+  auto load = [&](int s, int st) {
     const int h = g * grp + s / n_qt, qt = qt_lo + s % n_qt;
     const size_t lane_off = (size_t)(b * a.H + h) * nq;
-    const uint16_t* Qp = (const uint16_t*)a.Q + lane_off * D;
-    const uint16_t* Gp = (const uint16_t*)a.G + lane_off * D;
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, cc = c % CPR, q = qt * BQ + row;
-      qpre[u] = u32x4{0, 0, 0, 0};
-      gpre[u] = u32x4{0, 0, 0, 0};
-      if (q < nq) {
-        qpre[u] = *(const u32x4*)(Qp + (size_t)q * D + 8 * cc);
-        gpre[u] = *(const u32x4*)(Gp + (size_t)q * D + 8 * cc);
-      }
-    }
-    if (tid < 16) {
-      float lv[4], dvv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = qt * BQ + 4 * tid + r;
-        lv[r] = (q < nq) ? a.LSE[lane_off + q] : 0.f;
-        dvv[r] = (q < nq) ? a.Dws[lane_off + q] : 0.f;
-      }
-      lpre = f32x4{lv[0] * kLog2e, lv[1] * kLog2e, lv[2] * kLog2e, lv[3] * kLog2e};
-      dpre = f32x4{dvv[0], dvv[1], dvv[2], dvv[3]};
-    }
-  };
-  auto stash = [&](int st) {
     char ETS_LDS* qt_ = smem + st * STAGEB;
-    char ETS_LDS* gt_ = qt_ + TILEB;
-    float ETS_LDS* ls = (float ETS_LDS*)(gt_ + TILEB);
-    float ETS_LDS* ds = ls + BQ;
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, cc = c % CPR;
-      lds_st128(qt_, toff(row, 8 * cc, ROWB), qpre[u]);
-      lds_st128(gt_, toff(row, 8 * cc, ROWB), gpre[u]);
-    }
-    if (tid < 16) {
-      *(f32x4 ETS_LDS*)(ls + 4 * tid) = lpre;
-      *(f32x4 ETS_LDS*)(ds + 4 * tid) = dpre;
+    tile_to_lds<BQ, D, 4>(qt_, (const uint16_t*)a.Q + lane_off * D, qt * BQ, nq - 1, wave, lane);
+    tile_to_lds<BQ, D, 4>(qt_ + TILEB, (const uint16_t*)a.G + lane_off * D, qt * BQ, nq - 1, wave, lane);
+    if (wave == 0 && lane < 32) {
+      const float* src = (lane < 16 ? a.Lws : a.Dws) + lane_off + qt * BQ + 4 * (lane & 15);
+      __builtin_amdgcn_global_load_lds(src, (void ETS_LDS*)(qt_ + 2 * TILEB), 16, 0, 0);
     }
   };
 
   int s = (total > 0) ? (wg_nonempty(0) ? 0 : next_step(0)) : -1;
   int st = 0;
-  if (s >= 0) {
-    fetch(s);
-    stash(0);
-  }
+  if (s >= 0) load(s, 0);
+  wait_vm();
   __syncthreads();
   const float sl2 = a.scale_log2;
 
   while (s >= 0) {
     const int nxt = next_step(s);
-    if (nxt >= 0) fetch(nxt);
+    if (nxt >= 0) load(nxt, st ^ 1);
     const int h = g * grp + s / n_qt, qt = qt_lo + s % n_qt, qb0 = qt * BQ;
     const int lane_bh = b * a.H + h;
     const char ETS_LDS* qt_ = smem + st * STAGEB;
@@ -203,9 +180,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     const bool cbm = (cinfo & kCheckBlockMask) != 0;
 
     if (cls != kEmpty) {
-      vec8 pb[4], gb[4];  // P~ and gamma as B operands, k-steps of 16 queries
 #pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {
+      for (int mq = 0; mq < 2; ++mq) {  // 32 query rows at a time
         f32x16 sc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
@@ -216,57 +192,55 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
           const vec8 ga = as_vec8<E>(lds_b128(gt_, toff(32 * mq + l32, 16 * kk + 8 * h32, ROWB)));
           dp = E::mfma32(ga, vreg[kk], dp);
         }
+        // S and dP: lane = key, entries r = query rows 32mq + 8(r/4) + 4h32 + r%4
         uint32_t pw[8], gw[8];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qr = 32 * mq + 8 * g4 + 4 * h32;  // first of 4 query rows in the tile
           const f32x4 l4 = *(const f32x4 ETS_LDS*)(ls + qr);
           const f32x4 d4 = *(const f32x4 ETS_LDS*)(ds + qr);
-          const float lv[4] = {l4[0], l4[1], l4[2], l4[3]}, dvv[4] = {d4[0], d4[1], d4[2], d4[3]};
           unsigned allow = 0xFu, keep = 0xFu;
           if (cls == kPartial) allow = allowed4_rows(a.mask, qb0 + qr, key, nq, nk, cbm);
           if constexpr (DROP) keep = keep4_rows(a.drop, lane_bh, qb0 + qr, key);
-          float p[4], pk[4], gm[4];
+          float pk[4], gm[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float pv = fast_exp2(fmaf(sc[4 * g4 + r], sl2, -lv[r]));
-            if (!((allow >> r) & 1u)) pv = 0.f;
-            p[r] = pv;
+            const float pv = fast_exp2(fmaf(sc[4 * g4 + r], sl2, -l4[r]));
             float dpv = dp[4 * g4 + r];
+            bool kp = true;
             if constexpr (DROP) {
-              const bool kp = (keep >> r) & 1u;
+              kp = (keep >> r) & 1u;
               dpv = kp ? dpv * a.drop.inv_keep : 0.f;
-              pk[r] = kp ? pv : 0.f;
-            } else {
-              pk[r] = pv;
             }
-            gm[r] = pv * (dpv - dvv[r]);
+            const bool al = (allow >> r) & 1u;
+            pk[r] = (al && kp) ? pv : 0.f;
+            gm[r] = al ? pv * (dpv - d4[r]) : 0.f;
           }
           pw[2 * g4] = E::pack2(pk[0], pk[1]);
           pw[2 * g4 + 1] = E::pack2(pk[2], pk[3]);
           gw[2 * g4] = E::pack2(gm[0], gm[1]);
           gw[2 * g4 + 1] = E::pack2(gm[2], gm[3]);
         }
-        pb[2 * mq] = as_vec8<E>(u32x4{pw[0], pw[1], pw[2], pw[3]});
-        pb[2 * mq + 1] = as_vec8<E>(u32x4{pw[4], pw[5], pw[6], pw[7]});
-        gb[2 * mq] = as_vec8<E>(u32x4{gw[0], gw[1], gw[2], gw[3]});
-        gb[2 * mq + 1] = as_vec8<E>(u32x4{gw[4], gw[5], gw[6], gw[7]});
-      }
-      // dV^T += G^T P~,  dK^T += Q^T gamma  (contraction over the 64 queries)
+        // dV^T += G^T P~, dK^T += Q^T gamma over these 32 queries (2 k-steps)
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const int o = 4 * kk2;
+          const vec8 pb = as_vec8<E>(u32x4{pw[o], pw[o + 1], pw[o + 2], pw[o + 3]});
+          const vec8 gb = as_vec8<E>(u32x4{gw[o], gw[o + 1], gw[o + 2], gw[o + 3]});
+          const int r0 = 32 * mq + 16 * kk2 + 4 * h32;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int r0 = 16 * ks + 4 * h32, col0 = 32 * md + 16 * ((lane >> 4) & 1);
-          const vec8 gta = as_vec8<E>(lds_tr8(gt_, r0, r0 + 8, col0, ROWB, lane));
-          dv[md] = E::mfma32(gta, pb[ks], dv[md]);
-          const vec8 qta = as_vec8<E>(lds_tr8(qt_, r0, r0 + 8, col0, ROWB, lane));
-          dk[md] = E::mfma32(qta, gb[ks], dk[md]);
+          for (int md = 0; md < MD; ++md) {
+            const int col0 = 32 * md + 16 * ((lane >> 4) & 1);
+            const vec8 gta = as_vec8<E>(lds_tr8(gt_, r0, r0 + 8, col0, ROWB, lane));
+            dv[md] = E::mfma32(gta, pb, dv[md]);
+            const vec8 qta = as_vec8<E>(lds_tr8(qt_, r0, r0 + 8, col0, ROWB, lane));
+            dk[md] = E::mfma32(qta, gb, dk[md]);
+          }
         }
       }
     }
 
-    if (nxt >= 0) stash(st ^ 1);
+    wait_vm();
     __syncthreads();
     st ^= 1;
     s = nxt;
@@ -304,8 +278,6 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
   constexpr int MD = D / 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BK * ROWB;
-  constexpr int CPR = D / 8;
-  constexpr int LD = (BK * CPR) / 256;
   typedef typename E::vec8 vec8;
 
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * TILEB];
@@ -337,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
     qreg[kk] = as_vec8<E>(qv);
     greg[kk] = as_vec8<E>(gv);
   }
-  const float lse2 = (q < nq) ? a.LSE[(size_t)bh * nq + q] * kLog2e : 0.f;
+  const float lse2 = (q < nq) ? a.Lws[(size_t)bh * nq + q] : __builtin_huge_valf();
   const float dval = (q < nq) ? a.Dws[(size_t)bh * nq + q] : 0.f;
 
   f32x16 dq[MD];
@@ -359,42 +331,22 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
     return -1;
   };
 
-  u32x4 kpre[LD], vpre[LD];
-  auto fetch = [&](int jt) {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, cc = c % CPR, j = jt * BK + row;
-      kpre[u] = u32x4{0, 0, 0, 0};
-      vpre[u] = u32x4{0, 0, 0, 0};
-      if (j < nk) {
-        kpre[u] = *(const u32x4*)(Kp + (size_t)j * D + 8 * cc);
-        vpre[u] = *(const u32x4*)(Vp + (size_t)j * D + 8 * cc);
-      }
-    }
-  };
-  auto stash = [&](int stage) {
+  auto load = [&](int jt, int stage) {
     char ETS_LDS* kt = smem + stage * 2 * TILEB;
-    char ETS_LDS* vt = kt + TILEB;
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, cc = c % CPR;
-      lds_st128(kt, toff(row, 8 * cc, ROWB), kpre[u]);
-      lds_st128(vt, toff(row, 8 * cc, ROWB), vpre[u]);
-    }
+    tile_to_lds<BK, D, 4>(kt, Kp, jt * BK, nk - 1, wave, lane);
+    tile_to_lds<BK, D, 4>(kt + TILEB, Vp, jt * BK, nk - 1, wave, lane);
   };
 
   int jt = (jt_lo <= jt_hi && wg_nonempty(jt_lo)) ? jt_lo : next_tile(jt_lo);
   int stage = 0;
-  if (jt >= 0) {
-    fetch(jt);
-    stash(0);
-  }
+  if (jt >= 0) load(jt, 0);
+  wait_vm();
   __syncthreads();
   const float sl2 = a.scale_log2;
 
   while (jt >= 0) {
     const int nxt = next_tile(jt);
-    if (nxt >= 0) fetch(nxt);
+    if (nxt >= 0) load(nxt, stage ^ 1);
     const char ETS_LDS* kt = smem + stage * 2 * TILEB;
     const char ETS_LDS* vt = kt + TILEB;
     const int j0 = jt * BK;
@@ -430,11 +382,10 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
           float gm[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float pv = fast_exp2(fmaf(sc[mb][4 * g4 + r], sl2, -lse2));
-            if (!((allow >> r) & 1u)) pv = 0.f;
+            const float pv = fast_exp2(fmaf(sc[mb][4 * g4 + r], sl2, -lse2));
             float dpv = dp[mb][4 * g4 + r];
             if constexpr (DROP) dpv = ((keep >> r) & 1u) ? dpv * a.drop.inv_keep : 0.f;
-            gm[r] = pv * (dpv - dval);
+            gm[r] = ((allow >> r) & 1u) ? pv * (dpv - dval) : 0.f;
           }
           gw[mb][2 * g4] = E::pack2(gm[0], gm[1]);
           gw[mb][2 * g4 + 1] = E::pack2(gm[2], gm[3]);
@@ -453,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
       }
     }
 
-    if (nxt >= 0) stash(stage ^ 1);
+    wait_vm();
     __syncthreads();
     stage ^= 1;
     jt = nxt;
@@ -480,7 +431,7 @@ static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
   hipStream_t st = (hipStream_t)stream;
   if (phases & 1) {
     const int rows = a.B * a.H * a.nq;
-    const int prep_threads = rows * (D / 8);
+    const int prep_threads = (rows + 64) * (D / 8);
     ETS_TRY(launch((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows));
   }
   const int n_kblocks = (a.nk + 127) / 128;

@@ -38,8 +38,6 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
   constexpr int MD = D / 32;        // 32-row blocks of O^T
   constexpr int ROWB = D * 2;       // bytes per LDS tile row
   constexpr int TILEB = BK * ROWB;  // bytes per K or V tile
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int LD = (BK * CPR) / 256;  // chunks per thread per tile
   typedef typename E::vec8 vec8;
 
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * TILEB];
@@ -101,36 +99,18 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
     return -1;
   };
 
-  u32x4 kpre[LD], vpre[LD];
-  auto fetch = [&](int jt) {
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, cc = c % CPR, j = jt * BK + row;
-      kpre[u] = u32x4{0, 0, 0, 0};
-      vpre[u] = u32x4{0, 0, 0, 0};
-      if (j < nk) {
-        kpre[u] = *(const u32x4*)(Kp + (size_t)j * D + 8 * cc);
-        vpre[u] = *(const u32x4*)(Vp + (size_t)j * D + 8 * cc);
-      }
-    }
-  };
-  auto stash = [&](int stage) {
+  // K and V tiles go straight from HBM to LDS (rows past nk read row nk-1;
+  // those keys are masked as a ragged tile)
+  auto load = [&](int jt, int stage) {
     char ETS_LDS* kt = smem + stage * 2 * TILEB;
-    char ETS_LDS* vt = kt + TILEB;
-#pragma unroll
-    for (int u = 0; u < LD; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, cc = c % CPR;
-      lds_st128(kt, toff(row, 8 * cc, ROWB), kpre[u]);
-      lds_st128(vt, toff(row, 8 * cc, ROWB), vpre[u]);
-    }
+    tile_to_lds<BK, D, 4>(kt, Kp, jt * BK, nk - 1, wave, lane);
+    tile_to_lds<BK, D, 4>(kt + TILEB, Vp, jt * BK, nk - 1, wave, lane);
   };
 
   int jt = (jt_lo <= jt_hi && wg_nonempty(jt_lo)) ? jt_lo : next_tile(jt_lo);
   int stage = 0;
-  if (jt >= 0) {
-    fetch(jt);
-    stash(0);
-  }
+  if (jt >= 0) load(jt, 0);
+  wait_vm();
   __syncthreads();
 
   const float sl2 = a.scale_log2;
@@ -138,7 +118,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
 
   while (jt >= 0) {
     const int nxt = next_tile(jt);
-    if (nxt >= 0) fetch(nxt);
+    if (nxt >= 0) load(nxt, stage ^ 1);
     const char ETS_LDS* kt = smem + stage * 2 * TILEB;
     const char ETS_LDS* vt = kt + TILEB;
     const int j0 = jt * BK;
@@ -249,7 +229,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
       }
     }
 
-    if (nxt >= 0) stash(stage ^ 1);
+    wait_vm();
     __syncthreads();
     stage ^= 1;
     jt = nxt;

@@ -134,6 +134,34 @@ __device__ __forceinline__ u32x4 lds_tr8(const char ETS_LDS* base, int r0, int r
   return __builtin_bit_cast(u32x4, v);
 }
 
+// Direct global -> LDS copy of a tile of ROWS rows x W 16-bit elements into
+// the swizzled tile format (global_load_lds_dwordx4: lane l of a wave writes
+// 16 bytes at the instruction's LDS base + 16 l).  Each of the NWAVES waves
+// issues ROWS*W/8/64/NWAVES instructions; lane l of instruction k fills chunk
+// position 64k + l, so it fetches the logical chunk that the swizzle maps
+// there.  Rows past last_row are read from last_row instead (finite data; the
+// caller masks them), so no access leaves the tensor.  Completion is awaited
+// with wait_vm() before the barrier that publishes the tile.
+template <int ROWS, int W, int NWAVES>
+__device__ __forceinline__ void tile_to_lds(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row,
+                                            int wave, int lane) {
+  constexpr int CPR = W / 8;
+  constexpr int INSTS = ROWS * CPR / 64;
+  static_assert(INSTS % NWAVES == 0, "tile does not split evenly over the waves");
+  constexpr int PER_WAVE = INSTS / NWAVES;
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int inst = wave * PER_WAVE + u;
+    const int pos = inst * 64 + lane;
+    const int row = pos / CPR, pc = pos % CPR;
+    const int lc = pc ^ swz(row);
+    const int grow = min(row0 + row, last_row);
+    __builtin_amdgcn_global_load_lds(base + (size_t)grow * W + lc * 8, (void ETS_LDS*)(dst + inst * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ------------------------------------------------------------ lane exchange
 // permlane32_swap(x, x) hands every lane the value of lane (l ^ 32) in one of
 // its two results; combining both gives a full cross-half reduction.
@@ -222,8 +250,9 @@ enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2, kClassMask = 3, kCheckBloc
 // is mixed inside the rectangle and must be read per element.
 __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int ja, int jb, int nq, int nk) {
   if (ia >= nq || ja >= nk) return kEmpty;
+  // rows or keys past the end are present in the tile: mask them per element
+  int cls = (jb >= nk || ib >= nq) ? kPartial : kFull;
   if (ib >= nq) ib = nq - 1;
-  int cls = (jb >= nk) ? kPartial : kFull;
   if (jb >= nk) jb = nk - 1;
   if (m.causal) {
     if (ja > ib) return kEmpty;

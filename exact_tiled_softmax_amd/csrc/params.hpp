@@ -32,7 +32,8 @@ struct DenseArgs {
   void* out_Y;                        // forward output
   float* LSE;                         // forward output / backward input
   void* dQ; void* dK; void* dV;       // backward outputs
-  float* Dws;                         // backward workspace: D_i = G_i . Y_i  [B*H*nq]
+  float* Dws;                         // backward workspace: D_i = G_i . Y_i  [B*H*nq + 64]
+  float* Lws;                         // backward workspace: LSE_i log2(e)    [B*H*nq + 64]
   int B, H, Hkv, nq, nk, d, dv;
   float scale;                        // c
   float scale_log2;                   // c * log2(e)

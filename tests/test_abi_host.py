@@ -44,7 +44,7 @@ def test_status_strings():
 
 def test_workspace_sizes():
     import exact_tiled_softmax_amd as ets
-    assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 4, 16, 16, 2048, 2048, 128, 128) == 4 * 16 * 2048 * 4
+    assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 4, 16, 16, 2048, 2048, 128, 128) == 2 * (((4 * 16 * 2048 + 64) * 4 + 255) // 256 * 256)
     assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 0, 16, 16, 2048, 2048, 128, 128) == 0
     assert ets.attn_sparse_bwd_workspace_size(4096, 64, 16384, 576, 512, 2048) == 2 * 4096 * 64 * 4 + 16384 * 576 * 4
 
