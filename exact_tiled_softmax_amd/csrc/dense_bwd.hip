@@ -165,6 +165,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
   wait_vm();
   __syncthreads();
   const float sl2 = a.scale_log2;
+  const RowOps32<ROWB> rops(lane);
+  const TrOps32<ROWB> tops(lane);
 
   while (s >= 0) {
     const int nxt = next_step(s);
@@ -187,9 +189,9 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const vec8 qa = as_vec8<E>(lds_b128(qt_, toff(32 * mq + l32, 16 * kk + 8 * h32, ROWB)));
+          const vec8 qa = as_vec8<E>(lds_b128(qt_, rops.off(32 * mq, kk)));
           sc = E::mfma32(qa, kreg[kk], sc);
-          const vec8 ga = as_vec8<E>(lds_b128(gt_, toff(32 * mq + l32, 16 * kk + 8 * h32, ROWB)));
+          const vec8 ga = as_vec8<E>(lds_b128(gt_, rops.off(32 * mq, kk)));
           dp = E::mfma32(ga, vreg[kk], dp);
         }
         // S and dP: lane = key, entries r = query rows 32mq + 8(r/4) + 4h32 + r%4
@@ -227,13 +229,11 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
           const int o = 4 * kk2;
           const vec8 pb = as_vec8<E>(u32x4{pw[o], pw[o + 1], pw[o + 2], pw[o + 3]});
           const vec8 gb = as_vec8<E>(u32x4{gw[o], gw[o + 1], gw[o + 2], gw[o + 3]});
-          const int r0 = 32 * mq + 16 * kk2 + 4 * h32;
 #pragma unroll
           for (int md = 0; md < MD; ++md) {
-            const int col0 = 32 * md + 16 * ((lane >> 4) & 1);
-            const vec8 gta = as_vec8<E>(lds_tr8(gt_, r0, r0 + 8, col0, ROWB, lane));
+            const vec8 gta = as_vec8<E>(tops.read(gt_, 32 * mq + 16 * kk2, md));
             dv[md] = E::mfma32(gta, pb, dv[md]);
-            const vec8 qta = as_vec8<E>(lds_tr8(qt_, r0, r0 + 8, col0, ROWB, lane));
+            const vec8 qta = as_vec8<E>(tops.read(qt_, 32 * mq + 16 * kk2, md));
             dk[md] = E::mfma32(qta, gb, dk[md]);
           }
         }
@@ -343,6 +343,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
   wait_vm();
   __syncthreads();
   const float sl2 = a.scale_log2;
+  const RowOps32<ROWB> rops(lane);
+  const TrOps32<ROWB> tops(lane);
 
   while (jt >= 0) {
     const int nxt = next_tile(jt);
@@ -364,9 +366,9 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
       for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const vec8 ka = as_vec8<E>(lds_b128(kt, toff(32 * mb + l32, 16 * kk + 8 * h32, ROWB)));
+          const vec8 ka = as_vec8<E>(lds_b128(kt, rops.off(32 * mb, kk)));
           sc[mb] = E::mfma32(ka, qreg[kk], sc[mb]);
-          const vec8 va = as_vec8<E>(lds_b128(vt, toff(32 * mb + l32, 16 * kk + 8 * h32, ROWB)));
+          const vec8 va = as_vec8<E>(lds_b128(vt, rops.off(32 * mb, kk)));
           dp[mb] = E::mfma32(va, greg[kk], dp[mb]);
         }
       }
@@ -395,10 +397,9 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
       for (int ks = 0; ks < 4; ++ks) {
         const int mb = ks >> 1, o = (ks & 1) * 4;
         const vec8 gb = as_vec8<E>(u32x4{gw[mb][o], gw[mb][o + 1], gw[mb][o + 2], gw[mb][o + 3]});
-        const int r0 = 16 * ks + 4 * h32;
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-          const vec8 kta = as_vec8<E>(lds_tr8(kt, r0, r0 + 8, 32 * md + 16 * ((lane >> 4) & 1), ROWB, lane));
+          const vec8 kta = as_vec8<E>(tops.read(kt, 16 * ks, md));
           dq[md] = E::mfma32(kta, gb, dq[md]);
         }
       }

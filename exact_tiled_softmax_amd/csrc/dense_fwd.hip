@@ -8,13 +8,13 @@
 // that row's summary unchanged; at the end Y = z / l and LSE = m + ln l.
 //
 // Mapping onto CDNA4:
-//   * a workgroup owns BQ = 4 waves x 32*NB query rows of one (batch, head);
+//   * a workgroup owns BQ = NW waves x 32*NB query rows of one (batch, head);
 //     each wave keeps its Q rows in registers as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16, queries along lanes, keys along the
 //     accumulator rows), so a query's running max and sum live in one lane
 //     plus its partner lane l ^ 32;
-//   * K and V tiles of 64 keys are staged in LDS (double buffered, swizzled
-//     rows); the PV product is accumulated transposed, O^T += V^T P^T, with V^T
+//   * K and V tiles of 64 keys go straight from HBM into an LDS ring of 2-3
+//     stages (swizzled rows), so the next tiles load while one is used; the PV product is accumulated transposed, O^T += V^T P^T, with V^T
 //     read by ds_read_b64_tr_b16 and P^T fed straight from the S^T
 //     accumulators (no shuffles);
 //   * scores are kept in base 2 (c*log2 e folded into one FMA before
@@ -29,19 +29,20 @@ namespace ets {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <class E, int D, int NB, bool DROP>
-__global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const DenseArgs a, int n_qtiles) {
+template <class E, int D, int NB, int NW, int STAGES, bool DROP>
+__global__ __launch_bounds__(64 * NW, NB == 1 ? 2 : 1) void dense_fwd_kernel(const DenseArgs a, int n_qtiles) {
   constexpr int BK = 64;
   constexpr int NQW = 32 * NB;
-  constexpr int BQ = 4 * NQW;
+  constexpr int BQ = NW * NQW;
+  static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");  // launch passes STAGES * 2 * TILEB bytes
   constexpr int KS = D / 16;        // k-steps of the score contraction
   constexpr int MD = D / 32;        // 32-row blocks of O^T
   constexpr int ROWB = D * 2;       // bytes per LDS tile row
   constexpr int TILEB = BK * ROWB;  // bytes per K or V tile
   typedef typename E::vec8 vec8;
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * TILEB];
-  char ETS_LDS* smem = (char ETS_LDS*)smem_raw;
+  extern __shared__ __attribute__((aligned(16))) char smem_dyn[];  // STAGES x (K, V) tiles
+  char ETS_LDS* smem = (char ETS_LDS*)smem_dyn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
@@ -100,25 +101,35 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
   };
 
   // K and V tiles go straight from HBM to LDS (rows past nk read row nk-1;
-  // those keys are masked as a ragged tile)
+  // those keys are masked as a ragged tile), STAGES tiles in flight
+  constexpr int LOADS = 2 * (BK * D / 8 / 64) / NW;  // load instructions per wave per tile
   auto load = [&](int jt, int stage) {
     char ETS_LDS* kt = smem + stage * 2 * TILEB;
-    tile_to_lds<BK, D, 4>(kt, Kp, jt * BK, nk - 1, wave, lane);
-    tile_to_lds<BK, D, 4>(kt + TILEB, Vp, jt * BK, nk - 1, wave, lane);
+    tile_to_lds<BK, D, NW>(kt, Kp, jt * BK, nk - 1, wave, lane);
+    tile_to_lds<BK, D, NW>(kt + TILEB, Vp, jt * BK, nk - 1, wave, lane);
   };
 
-  int jt = (jt_lo <= jt_hi && wg_nonempty(jt_lo)) ? jt_lo : next_tile(jt_lo);
-  int stage = 0;
-  if (jt >= 0) load(jt, 0);
+  // tiles[0] is the tile in use, tiles[1 .. STAGES-2] are already in flight
+  int tiles[STAGES - 1];
+  tiles[0] = (jt_lo <= jt_hi && wg_nonempty(jt_lo)) ? jt_lo : next_tile(jt_lo);
+#pragma unroll
+  for (int k = 1; k < STAGES - 1; ++k) tiles[k] = (tiles[k - 1] >= 0) ? next_tile(tiles[k - 1]) : -1;
+#pragma unroll
+  for (int k = 0; k < STAGES - 1; ++k)
+    if (tiles[k] >= 0) load(tiles[k], k);
   wait_vm();
   __syncthreads();
+  int stage = 0;
 
   const float sl2 = a.scale_log2;
   const int lane_bh = bh;
+  const RowOps32<ROWB> kops(lane);
+  const TrOps32<ROWB> vops(lane);
 
-  while (jt >= 0) {
-    const int nxt = next_tile(jt);
-    if (nxt >= 0) load(nxt, stage ^ 1);
+  while (tiles[0] >= 0) {
+    const int jt = tiles[0];
+    const int tn = (tiles[STAGES - 2] >= 0) ? next_tile(tiles[STAGES - 2]) : -1;
+    if (tn >= 0) load(tn, stage == 0 ? STAGES - 1 : stage - 1);  // the stage read last iteration
     const char ETS_LDS* kt = smem + stage * 2 * TILEB;
     const char ETS_LDS* vt = kt + TILEB;
     const int j0 = jt * BK;
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
       for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const vec8 ka = as_vec8<E>(lds_b128(kt, toff(32 * mb + l32, 16 * kk + 8 * h32, ROWB)));
+          const vec8 ka = as_vec8<E>(lds_b128(kt, kops.off(32 * mb, kk)));
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) s[mb][nb] = E::mfma32(ka, qreg[nb][kk], s[mb][nb]);
         }
@@ -221,18 +232,20 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
       for (int md = 0; md < MD; ++md) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int r0 = 16 * ks + 4 * h32;
-          const vec8 va = as_vec8<E>(lds_tr8(vt, r0, r0 + 8, 32 * md + 16 * ((lane >> 4) & 1), ROWB, lane));
+          const vec8 va = as_vec8<E>(vops.read(vt, 16 * ks, md));
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) oacc[md][nb] = E::mfma32(va, pb[nb][ks], oacc[md][nb]);
         }
       }
     }
 
-    wait_vm();
+    // the next tile must be complete; later ones may stay in flight
+    if (tn >= 0) wait_vm_n<(STAGES - 2) * LOADS>(); else wait_vm();
     __syncthreads();
-    stage ^= 1;
-    jt = nxt;
+#pragma unroll
+    for (int k = 0; k < STAGES - 2; ++k) tiles[k] = tiles[k + 1];
+    tiles[STAGES - 2] = tn;
+    stage = (stage == STAGES - 1) ? 0 : stage + 1;
   }
 
   // ---- epilogue: Y = z / l, LSE = (m + log2 l) ln 2
@@ -260,15 +273,16 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void dense_fwd_kernel(const D
   }
 }
 
-template <class E, int D, int NB>
+template <class E, int D, int NB, int NW, int STAGES>
 static int launch_fwd_t(const DenseArgs& a, void* stream) {
-  constexpr int BQ = 4 * 32 * NB;
+  constexpr int BQ = NW * 32 * NB;
+  constexpr int LDS = STAGES * 2 * 64 * D * 2;
   const int n_qtiles = (a.nq + BQ - 1) / BQ;
-  dim3 grid(n_qtiles * a.B * a.H), block(256);
+  dim3 grid(n_qtiles * a.B * a.H), block(64 * NW);
   if (a.drop.enabled)
-    ETS_TRY(launch((dense_fwd_kernel<E, D, NB, true>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
+    ETS_TRY(launch((dense_fwd_kernel<E, D, NB, NW, STAGES, true>), grid, block, LDS, (hipStream_t)stream, a, n_qtiles));
   else
-    ETS_TRY(launch((dense_fwd_kernel<E, D, NB, false>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
+    ETS_TRY(launch((dense_fwd_kernel<E, D, NB, NW, STAGES, false>), grid, block, LDS, (hipStream_t)stream, a, n_qtiles));
   return 0;
 }
 
@@ -276,11 +290,11 @@ bool dense_mfma_supported(int d, int dv) { return d == dv && (d == 64 || d == 12
 
 int launch_dense_fwd(const DenseArgs& a, Dt dt, void* stream) {
   if (dt == Dt::BF16) {
-    if (a.d == 128) return launch_fwd_t<BF16, 128, 1>(a, stream);
-    return launch_fwd_t<BF16, 64, 1>(a, stream);
+    if (a.d == 128) return launch_fwd_t<BF16, 128, 1, 4, 2>(a, stream);
+    return launch_fwd_t<BF16, 64, 1, 4, 3>(a, stream);
   }
-  if (a.d == 128) return launch_fwd_t<F16, 128, 1>(a, stream);
-  return launch_fwd_t<F16, 64, 1>(a, stream);
+  if (a.d == 128) return launch_fwd_t<F16, 128, 1, 4, 2>(a, stream);
+  return launch_fwd_t<F16, 64, 1, 4, 3>(a, stream);
 }
 
 }  // namespace ets

@@ -93,17 +93,39 @@ __device__ __forceinline__ typename E::vec8 as_vec8(u32x4 u) {
 
 // ------------------------------------------------------------ LDS tile format
 // A tile is row-major with a fixed byte stride per row; its 16-byte chunks are
-// XOR-swizzled by swz(row) within each group of 8 chunks.  The swizzle makes
-// both access patterns of the kernels conflict-free:
-//   * 16-byte reads of one chunk column by 8 consecutive rows (MFMA operand
+// XOR-swizzled by a function of the row within groups of MASK+1 chunks.  The
+// swizzle depends on the row width (CDNA4's LDS serves 256 bytes per clock
+// from 64 banks): it makes both access patterns of the kernels conflict-free
+// or nearly so (measured on MI355X):
+//   * 16-byte reads of one chunk column by 16 consecutive rows (MFMA operand
 //     rows), and
 //   * transpose reads, where 16 lanes read 4 consecutive rows (starting at a
 //     multiple of 4) x 32 contiguous bytes.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Every swizzle below depends on the row modulo 16 only.
+template <int ROWB> struct Swizzle;
+template <> struct Swizzle<256> {  // 128 16-bit columns
+  static constexpr int MASK = 15;
+  static __device__ __forceinline__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+template <> struct Swizzle<128> {  // 64 16-bit columns: two rows share a bank line
+  static constexpr int MASK = 7;
+  static __device__ __forceinline__ int f(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+};
+template <> struct Swizzle<1152> {  // 576 16-bit columns: alternate rows start half a bank line apart
+  static constexpr int MASK = 7;
+  static __device__ __forceinline__ int f(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+};
 
-// byte offset of element (row, col) of a 16-bit tile
-__device__ __forceinline__ int toff(int row, int col, int rowbytes) {
-  return row * rowbytes + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
+template <int ROWB>
+__device__ __forceinline__ int phys_chunk(int row, int chunk) {
+  constexpr int M = Swizzle<ROWB>::MASK;
+  return (chunk & ~M) | ((chunk & M) ^ Swizzle<ROWB>::f(row));
+}
+
+// byte offset of element (row, col) of a 16-bit tile with ROWB bytes per row
+template <int ROWB>
+__device__ __forceinline__ int toff(int row, int col) {
+  return row * ROWB + (phys_chunk<ROWB>(row, col >> 3) << 4) + ((col & 7) << 1);
 }
 
 __device__ __forceinline__ u32x4 lds_b128(const char ETS_LDS* base, int off) {
@@ -124,12 +146,12 @@ __device__ __forceinline__ s16x4 lds_tr4(const char ETS_LDS* base, int off) {
 // An MFMA operand holding 8 elements of one column (the "m" or "n" index
 // col0 + lane%32 for 32x32 shapes) along 8 rows: the lane's k-slots 0..3 are
 // rows r0 .. r0+3 and slots 4..7 are rows r1 .. r1+3.
-__device__ __forceinline__ u32x4 lds_tr8(const char ETS_LDS* base, int r0, int r1, int col0,
-                                         int rowbytes, int lane) {
+template <int ROWB>
+__device__ __forceinline__ u32x4 lds_tr8(const char ETS_LDS* base, int r0, int r1, int col0, int lane) {
   const int i = lane & 15;
   const int col = col0 + 4 * (i & 3);
-  s16x4 a = lds_tr4(base, toff(r0 + (i >> 2), col, rowbytes));
-  s16x4 b = lds_tr4(base, toff(r1 + (i >> 2), col, rowbytes));
+  s16x4 a = lds_tr4(base, toff<ROWB>(r0 + (i >> 2), col));
+  s16x4 b = lds_tr4(base, toff<ROWB>(r1 + (i >> 2), col));
   s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(u32x4, v);
 }
@@ -154,13 +176,98 @@ __device__ __forceinline__ void tile_to_lds(char ETS_LDS* dst, const uint16_t* b
     const int inst = wave * PER_WAVE + u;
     const int pos = inst * 64 + lane;
     const int row = pos / CPR, pc = pos % CPR;
-    const int lc = pc ^ swz(row);
+    const int lc = phys_chunk<2 * W>(row, pc);  // the swizzle is an involution
     const int grow = min(row0 + row, last_row);
     __builtin_amdgcn_global_load_lds(base + (size_t)grow * W + lc * 8, (void ETS_LDS*)(dst + inst * 1024), 16, 0, 0);
   }
 }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (the loads of later tiles stay in flight).
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-lane byte offsets of the MFMA operand reads.  toff() mixes lane terms
+// and loop indices through the swizzle XOR; these split it into a few
+// per-lane bases (computed once with toff itself) plus terms that are
+// compile-time constants once the loops are unrolled, so every read is
+// base + immediate offset.  The split is exact because the swizzles depend on
+// the row modulo 16 and the base rows R passed in are multiples of 16, and
+// because each XOR group of MASK+1 chunks is visited whole.
+
+// 32x32x16 operand rows: lane reads row R + lane%32, elements 16kk + 8(lane/32) .. +7
+template <int ROWB>
+struct RowOps32 {
+  static constexpr int NB = (Swizzle<ROWB>::MASK + 1) / 2;  // k-steps per XOR group
+  int b[NB];
+  __device__ __forceinline__ explicit RowOps32(int lane) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) b[k] = toff<ROWB>(lane & 31, 16 * k + 8 * (lane >> 5));
+  }
+  __device__ __forceinline__ int off(int R, int kk) const {
+    return b[kk % NB] + (kk / NB) * (Swizzle<ROWB>::MASK + 1) * 16 + R * ROWB;
+  }
+};
+
+// 32x32x16 transpose operand: column 32md + lane%32, rows R + 4(lane/32) + 0..3
+// (k-slots 0..3) and R + 8 + 4(lane/32) + 0..3 (k-slots 4..7)
+template <int ROWB>
+struct TrOps32 {
+  static constexpr int NP = (Swizzle<ROWB>::MASK + 1) / 4;  // md blocks per XOR group
+  int t[NP][2];
+  __device__ __forceinline__ explicit TrOps32(int lane) {
+    const int i = lane & 15, g1 = (lane >> 4) & 1, h = lane >> 5;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec)
+        t[p][sec] = toff<ROWB>(4 * h + 8 * sec + (i >> 2), 32 * p + 16 * g1 + 4 * (i & 3));
+  }
+  __device__ __forceinline__ u32x4 read(const char ETS_LDS* base, int R, int md) const {
+    const int o = (md / NP) * (Swizzle<ROWB>::MASK + 1) * 16 + R * ROWB;
+    const s16x4 a = lds_tr4(base, t[md % NP][0] + o), c = lds_tr4(base, t[md % NP][1] + o);
+    const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    return __builtin_bit_cast(u32x4, v);
+  }
+};
+
+// 16x16x32 operand rows: lane reads row R + lane%16, elements 32kk + 8(lane/16) .. +7
+template <int ROWB>
+struct RowOps16 {
+  static constexpr int NB = (Swizzle<ROWB>::MASK + 1) / 4;
+  int b[NB];
+  __device__ __forceinline__ explicit RowOps16(int lane) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) b[k] = toff<ROWB>(lane & 15, 32 * k + 8 * (lane >> 4));
+  }
+  __device__ __forceinline__ int off(int R, int kk) const {
+    return b[kk % NB] + (kk / NB) * (Swizzle<ROWB>::MASK + 1) * 16 + R * ROWB;
+  }
+};
+
+// 16x16x32 transpose operand: column 16m + lane%16, rows 4(lane/16) + 0..3
+// (k-slots 0..3) and 16 + 4(lane/16) + 0..3 (k-slots 4..7)
+template <int ROWB>
+struct TrOps16 {
+  static constexpr int NP = (Swizzle<ROWB>::MASK + 1) / 2;
+  int t[NP];
+  __device__ __forceinline__ explicit TrOps16(int lane) {
+    const int i = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) t[p] = toff<ROWB>(4 * G + (i >> 2), 16 * p + 4 * (i & 3));
+  }
+  __device__ __forceinline__ u32x4 read(const char ETS_LDS* base, int m) const {
+    const int o = t[m % NP] + (m / NP) * (Swizzle<ROWB>::MASK + 1) * 16;
+    const s16x4 a = lds_tr4(base, o), c = lds_tr4(base, o + 16 * ROWB);
+    const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    return __builtin_bit_cast(u32x4, v);
+  }
+};
 
 // ------------------------------------------------------------ lane exchange
 // permlane32_swap(x, x) hands every lane the value of lane (l ^ 32) in one of

@@ -67,7 +67,7 @@ struct Gather {
 #pragma unroll
     for (int v = 0; v < sp::NCH; ++v) {
       const int c = tid + 256 * v, row = c / sp::CPR, cc = c % sp::CPR;
-      lds_st128(buf, toff(row, 8 * cc, sp::ROWB), pre[v]);
+      lds_st128(buf, toff<sp::ROWB>(row, 8 * cc), pre[v]);
     }
   }
 };
@@ -84,8 +84,8 @@ __device__ __forceinline__ float grp4_sum(float x) {
 
 // S^T = K_tile Q_h^T for this wave's 16 heads: s[mb][i] is key 16mb + 4(lane/16) + i
 template <class E>
-__device__ __forceinline__ void scores(const char ETS_LDS* kt, const typename E::vec8* qreg, int lane, f32x4 s[2]) {
-  const int G = lane >> 4, l16 = lane & 15;
+__device__ __forceinline__ void scores(const char ETS_LDS* kt, const typename E::vec8* qreg,
+                                       const RowOps16<sp::ROWB>& rops, f32x4 s[2]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -94,19 +94,15 @@ __device__ __forceinline__ void scores(const char ETS_LDS* kt, const typename E:
   for (int kk = 0; kk < sp::KSQ; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const typename E::vec8 ka = as_vec8<E>(lds_b128(kt, toff(16 * mb + l16, 32 * kk + 8 * G, sp::ROWB)));
+      const typename E::vec8 ka = as_vec8<E>(lds_b128(kt, rops.off(16 * mb, kk)));
       s[mb] = E::mfma16(ka, qreg[kk], s[mb]);
     }
   }
 }
 
-// An MFMA operand whose k-slots are the tile's keys 4G..4G+3, 16+4G..16+4G+3
-// (the order the S^T accumulators hold them in), taken from column block
-// col0 .. col0+15 of the tile by transpose reads.
-__device__ __forceinline__ u32x4 tile_cols_tr(const char ETS_LDS* kt, int col0, int lane) {
-  const int G = lane >> 4;
-  return lds_tr8(kt, 4 * G, 16 + 4 * G, col0, sp::ROWB, lane);
-}
+// Operands whose k-slots are the tile's keys 4G..4G+3, 16+4G..16+4G+3 (the
+// order the S^T accumulators hold them in) come from TrOps16::read(tile, m):
+// column block 16m .. 16m+15 of the tile by transpose reads.
 
 // ------------------------------------------------------------------ forward
 template <class E>
@@ -138,6 +134,8 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
   const float sl2 = a.scale_log2;
 
   Gather gat;
+  const RowOps16<ROWB> rops(lane);
+  const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
     gat.fetch(KV, idx_t, L, 0, tid);
@@ -150,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
 
     f32x4 s[2];
-    scores<E>(kt, qreg, lane, s);
+    scores<E>(kt, qreg, rops, s);
     const bool ragged = u0 + BK > L;
     if (ragged) {
 #pragma unroll
@@ -190,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
                                      E::pack2(p[1][0], p[1][1]), E::pack2(p[1][2], p[1][3])});
 #pragma unroll
     for (int m = 0; m < MV; ++m) {
-      const vec8 va = as_vec8<E>(tile_cols_tr(kt, 16 * m, lane));
+      const vec8 va = as_vec8<E>(tops.read(kt, m));
       oacc[m] = E::mfma16(va, pb, oacc[m]);
     }
     if (it + 1 < ntiles) gat.stash(smem + ((it + 1) & 1) * TILEB, tid);
@@ -245,13 +243,14 @@ __global__ __launch_bounds__(256) void sparse_bwd_prep_kernel(const SparseArgs a
 // wave's 16 heads (k-slot order of tile_cols_tr), as packed MFMA operands.
 template <class E>
 __device__ __forceinline__ void recompute_p_ds(const char ETS_LDS* kt, const typename E::vec8* qreg,
-                                               const typename E::vec8* greg, int lane, int u0, int L,
+                                               const typename E::vec8* greg, const RowOps16<sp::ROWB>& rops,
+                                               int lane, int u0, int L,
                                                float sl2, float lse2, float Dv, typename E::vec8& pb,
                                                typename E::vec8& db) {
   using namespace sp;
-  const int G = lane >> 4, l16 = lane & 15;
+  const int G = lane >> 4;
   f32x4 s[2];
-  scores<E>(kt, qreg, lane, s);
+  scores<E>(kt, qreg, rops, s);
   f32x4 dp[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -262,7 +261,7 @@ __device__ __forceinline__ void recompute_p_ds(const char ETS_LDS* kt, const typ
   for (int kk = 0; kk < KSV; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const typename E::vec8 va = as_vec8<E>(lds_b128(kt, toff(16 * mb + l16, 32 * kk + 8 * G, ROWB)));
+      const typename E::vec8 va = as_vec8<E>(lds_b128(kt, rops.off(16 * mb, kk)));
       dp[mb] = E::mfma16(va, greg[kk], dp[mb]);
     }
   }
@@ -317,6 +316,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
     for (int r = 0; r < 4; ++r) dq[m][r] = 0.f;
 
   Gather gat;
+  const RowOps16<ROWB> rops(lane);
+  const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
     gat.fetch(KV, idx_t, L, 0, tid);
@@ -328,11 +329,11 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
     if (it + 1 < ntiles) gat.fetch(KV, idx_t, L, u0 + BK, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
     vec8 pb, db;
-    recompute_p_ds<E>(kt, qreg, greg, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
+    recompute_p_ds<E>(kt, qreg, greg, rops, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
-      const vec8 ka = as_vec8<E>(tile_cols_tr(kt, 16 * m, lane));
+      const vec8 ka = as_vec8<E>(tops.read(kt, m));
       dq[m] = E::mfma16(ka, db, dq[m]);
     }
     if (it + 1 < ntiles) gat.stash(smem + ((it + 1) & 1) * TILEB, tid);
@@ -395,19 +396,19 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
     const uint16_t* Qt = (const uint16_t*)a.Q + (size_t)t * H * DQK;
     for (int c = tid; c < H * CPR; c += 256) {
       const int r = c / CPR, cc = c % CPR;
-      lds_st128(smem, toff(r, 8 * cc, ROWB), *(const u32x4*)(Qt + (size_t)r * DQK + 8 * cc));
+      lds_st128(smem, toff<ROWB>(r, 8 * cc), *(const u32x4*)(Qt + (size_t)r * DQK + 8 * cc));
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        qt[m][ks] = as_vec8<E>(lds_tr8(smem, 32 * ks + 8 * G, 32 * ks + 8 * G + 4, c0w + 16 * m, ROWB, lane));
+        qt[m][ks] = as_vec8<E>(lds_tr8<ROWB>(smem, 32 * ks + 8 * G, 32 * ks + 8 * G + 4, c0w + 16 * m, lane));
     __syncthreads();
     const uint16_t* Gt = (const uint16_t*)a.dO + (size_t)t * H * DV;
     for (int c = tid; c < H * (DV / 8); c += 256) {
       const int r = c / (DV / 8), cc = c % (DV / 8);
-      lds_st128(smem, toff(r, 8 * cc, ROWB), *(const u32x4*)(Gt + (size_t)r * DV + 8 * cc));
+      lds_st128(smem, toff<ROWB>(r, 8 * cc), *(const u32x4*)(Gt + (size_t)r * DV + 8 * cc));
     }
     __syncthreads();
 #pragma unroll
@@ -415,13 +416,15 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int col = c0w + 16 * m;
-        gt[m][ks] = (col < DV) ? as_vec8<E>(lds_tr8(smem, 32 * ks + 8 * G, 32 * ks + 8 * G + 4, col, ROWB, lane))
+        gt[m][ks] = (col < DV) ? as_vec8<E>(lds_tr8<ROWB>(smem, 32 * ks + 8 * G, 32 * ks + 8 * G + 4, col, lane))
                                : as_vec8<E>(u32x4{0, 0, 0, 0});
       }
     __syncthreads();
   }
 
   Gather gat;
+  const RowOps16<ROWB> rops(lane);
+  const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
     gat.fetch(KV, idx_t, L, 0, tid);
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
     if (it + 1 < ntiles) gat.fetch(KV, idx_t, L, u0 + BK, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
     vec8 pb, db;
-    recompute_p_ds<E>(kt, qreg, greg, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
+    recompute_p_ds<E>(kt, qreg, greg, rops, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
     // P and dS of this wave's heads -> LDS [key][head]
     {
       const u32x4 pw = __builtin_bit_cast(u32x4, pb), dw = __builtin_bit_cast(u32x4, db);
