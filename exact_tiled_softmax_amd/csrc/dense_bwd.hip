@@ -74,17 +74,8 @@ __device__ __forceinline__ unsigned keep4_rows(const DropArgs& d, int lane_bh, i
   return out;
 }
 
-// Allowed bits of query rows i0..i0+3 (bit r <-> row i0 + r) for key j.
-__device__ __forceinline__ unsigned allowed4_rows(const MaskArgs& m, int i0, int j, int nq, int nk,
-                                                  bool check_bm) {
-  unsigned bits = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) bits |= (allowed1(m, i0 + r, j, nq, nk, check_bm) ? 1u : 0u) << r;
-  return bits;
-}
-
 // --------------------------------------------------------------------- dK, dV
-template <class E, int D, bool DROP>
+template <class E, int D, int MK, bool DROP>
 __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs a) {
   constexpr int BQ = 64;             // query rows per tile
   constexpr int KS = D / 16;
@@ -97,7 +88,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB];
   char ETS_LDS* smem = (char ETS_LDS*)smem_raw;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h32 = lane >> 5, l32 = lane & 31;
   const int nq = a.nq, nk = a.nk;
   const int BG = a.B * a.Hkv;
@@ -138,7 +130,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
 
   auto wg_nonempty = [&](int step) {
     const int qt = qt_lo + step % n_qt;
-    return classify(a.mask, qt * BQ, qt * BQ + BQ - 1, k0, k0 + 127, nq, nk) != kEmpty;
+    return classify<MK>(a.mask, qt * BQ, qt * BQ + BQ - 1, k0, k0 + 127, nq, nk) != kEmpty;
   };
   auto next_step = [&](int s) {
     for (++s; s < total; ++s)
@@ -177,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     const char ETS_LDS* gt_ = qt_ + TILEB;
     const float ETS_LDS* ls = (const float ETS_LDS*)(gt_ + TILEB);
     const float ETS_LDS* ds = ls + BQ;
-    const int cinfo = classify(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nq, nk);
+    const int cinfo = classify<MK>(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nq, nk);
     const int cls = cinfo & kClassMask;
     const bool cbm = (cinfo & kCheckBlockMask) != 0;
 
@@ -187,12 +179,18 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         f32x16 sc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+        // Q and G operands read one k-step ahead of their MFMAs
+        vec8 qa[2], ga[2];
+        qa[0] = as_vec8<E>(lds_b128(qt_, rops.off(32 * mq, 0)));
+        ga[0] = as_vec8<E>(lds_b128(gt_, rops.off(32 * mq, 0)));
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const vec8 qa = as_vec8<E>(lds_b128(qt_, rops.off(32 * mq, kk)));
-          sc = E::mfma32(qa, kreg[kk], sc);
-          const vec8 ga = as_vec8<E>(lds_b128(gt_, rops.off(32 * mq, kk)));
-          dp = E::mfma32(ga, vreg[kk], dp);
+          if (kk + 1 < KS) {
+            qa[(kk + 1) & 1] = as_vec8<E>(lds_b128(qt_, rops.off(32 * mq, kk + 1)));
+            ga[(kk + 1) & 1] = as_vec8<E>(lds_b128(gt_, rops.off(32 * mq, kk + 1)));
+          }
+          sc = E::mfma32(qa[kk & 1], kreg[kk], sc);
+          dp = E::mfma32(ga[kk & 1], vreg[kk], dp);
         }
         // S and dP: lane = key, entries r = query rows 32mq + 8(r/4) + 4h32 + r%4
         uint32_t pw[8], gw[8];
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
           const f32x4 l4 = *(const f32x4 ETS_LDS*)(ls + qr);
           const f32x4 d4 = *(const f32x4 ETS_LDS*)(ds + qr);
           unsigned allow = 0xFu, keep = 0xFu;
-          if (cls == kPartial) allow = allowed4_rows(a.mask, qb0 + qr, key, nq, nk, cbm);
+          if (cls == kPartial) allow = allowed4_rows<MK>(a.mask, qb0 + qr, key, nq, nk, cbm);
           if constexpr (DROP) keep = keep4_rows(a.drop, lane_bh, qb0 + qr, key);
           float pk[4], gm[4];
 #pragma unroll
@@ -223,19 +221,29 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
           gw[2 * g4] = E::pack2(gm[0], gm[1]);
           gw[2 * g4 + 1] = E::pack2(gm[2], gm[3]);
         }
-        // dV^T += G^T P~, dK^T += Q^T gamma over these 32 queries (2 k-steps)
+        // dV^T += G^T P~, dK^T += Q^T gamma over these 32 queries (2 k-steps);
+        // transpose operands read one step ahead
+        vec8 pb[2], gb[2];
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
           const int o = 4 * kk2;
-          const vec8 pb = as_vec8<E>(u32x4{pw[o], pw[o + 1], pw[o + 2], pw[o + 3]});
-          const vec8 gb = as_vec8<E>(u32x4{gw[o], gw[o + 1], gw[o + 2], gw[o + 3]});
+          pb[kk2] = as_vec8<E>(u32x4{pw[o], pw[o + 1], pw[o + 2], pw[o + 3]});
+          gb[kk2] = as_vec8<E>(u32x4{gw[o], gw[o + 1], gw[o + 2], gw[o + 3]});
+        }
+        constexpr int NT = 2 * MD;
+        vec8 gta[2], qta[2];
+        gta[0] = as_vec8<E>(tops.read(gt_, 32 * mq, 0));
+        qta[0] = as_vec8<E>(tops.read(qt_, 32 * mq, 0));
 #pragma unroll
-          for (int md = 0; md < MD; ++md) {
-            const vec8 gta = as_vec8<E>(tops.read(gt_, 32 * mq + 16 * kk2, md));
-            dv[md] = E::mfma32(gta, pb, dv[md]);
-            const vec8 qta = as_vec8<E>(tops.read(qt_, 32 * mq + 16 * kk2, md));
-            dk[md] = E::mfma32(qta, gb, dk[md]);
+        for (int t = 0; t < NT; ++t) {
+          const int kk2 = t / MD, md = t % MD;
+          if (t + 1 < NT) {
+            const int R1 = 32 * mq + 16 * ((t + 1) / MD), md1 = (t + 1) % MD;
+            gta[(t + 1) & 1] = as_vec8<E>(tops.read(gt_, R1, md1));
+            qta[(t + 1) & 1] = as_vec8<E>(tops.read(qt_, R1, md1));
           }
+          dv[md] = E::mfma32(gta[t & 1], pb[kk2], dv[md]);
+          dk[md] = E::mfma32(qta[t & 1], gb[kk2], dk[md]);
         }
       }
     }
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
 }
 
 // --------------------------------------------------------------------- dQ
-template <class E, int D, bool DROP>
+template <class E, int D, int MK, bool DROP>
 __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a, int n_qtiles) {
   constexpr int BK = 64;
   constexpr int NQW = 32;
@@ -283,7 +291,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * TILEB];
   char ETS_LDS* smem = (char ETS_LDS*)smem_raw;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h32 = lane >> 5, l32 = lane & 31;
   const int BH = a.B * a.H;
   const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
   if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
   if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
   auto wg_nonempty = [&](int jt) {
-    return classify(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
+    return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
   };
   auto next_tile = [&](int jt) {
     for (++jt; jt <= jt_hi; ++jt)
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
     const char ETS_LDS* kt = smem + stage * 2 * TILEB;
     const char ETS_LDS* vt = kt + TILEB;
     const int j0 = jt * BK;
-    const int cinfo = classify(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
+    const int cinfo = classify<MK>(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
     const int cls = cinfo & kClassMask;
     const bool cbm = (cinfo & kCheckBlockMask) != 0;
 
@@ -362,14 +371,26 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sc[mb][r] = 0.f; dp[mb][r] = 0.f; }
+      // K and V operands read one k-step ahead of their MFMAs
+      vec8 ka[2][2], va[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        ka[0][mb] = as_vec8<E>(lds_b128(kt, rops.off(32 * mb, 0)));
+        va[0][mb] = as_vec8<E>(lds_b128(vt, rops.off(32 * mb, 0)));
+      }
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            ka[(kk + 1) & 1][mb] = as_vec8<E>(lds_b128(kt, rops.off(32 * mb, kk + 1)));
+            va[(kk + 1) & 1][mb] = as_vec8<E>(lds_b128(vt, rops.off(32 * mb, kk + 1)));
+          }
+        }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const vec8 ka = as_vec8<E>(lds_b128(kt, rops.off(32 * mb, kk)));
-          sc[mb] = E::mfma32(ka, qreg[kk], sc[mb]);
-          const vec8 va = as_vec8<E>(lds_b128(vt, rops.off(32 * mb, kk)));
-          dp[mb] = E::mfma32(va, greg[kk], dp[mb]);
+          sc[mb] = E::mfma32(ka[kk & 1][mb], qreg[kk], sc[mb]);
+          dp[mb] = E::mfma32(va[kk & 1][mb], greg[kk], dp[mb]);
         }
       }
       uint32_t gw[2][8];
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
         for (int g4 = 0; g4 < 4; ++g4) {
           const int jj = j0 + 32 * mb + 8 * g4 + 4 * h32;
           unsigned allow = 0xFu, keep = 0xFu;
-          if (cls == kPartial) allow = allowed4(a.mask, q, jj, nq, nk, cbm);
+          if (cls == kPartial) allow = allowed4<MK>(a.mask, q, jj, nq, nk, cbm);
           if constexpr (DROP) keep = keep4(a.drop, bh, q, jj);
           float gm[4];
 #pragma unroll
@@ -392,16 +413,21 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
           gw[mb][2 * g4] = E::pack2(gm[0], gm[1]);
           gw[mb][2 * g4 + 1] = E::pack2(gm[2], gm[3]);
         }
-      // dQ^T += K^T gamma^T
+      // dQ^T += K^T gamma^T (K^T operands read one step ahead)
+      vec8 gbs[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int mb = ks >> 1, o = (ks & 1) * 4;
-        const vec8 gb = as_vec8<E>(u32x4{gw[mb][o], gw[mb][o + 1], gw[mb][o + 2], gw[mb][o + 3]});
+        gbs[ks] = as_vec8<E>(u32x4{gw[mb][o], gw[mb][o + 1], gw[mb][o + 2], gw[mb][o + 3]});
+      }
+      constexpr int NT = 4 * MD;
+      vec8 kta[2];
+      kta[0] = as_vec8<E>(tops.read(kt, 0, 0));
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const vec8 kta = as_vec8<E>(tops.read(kt, 16 * ks, md));
-          dq[md] = E::mfma32(kta, gb, dq[md]);
-        }
+      for (int t = 0; t < NT; ++t) {
+        const int ks = t / MD, md = t % MD;
+        if (t + 1 < NT) kta[(t + 1) & 1] = as_vec8<E>(tops.read(kt, 16 * ((t + 1) / MD), (t + 1) % MD));
+        dq[md] = E::mfma32(kta[t & 1], gbs[ks], dq[md]);
       }
     }
 
@@ -428,6 +454,32 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
 }
 
 template <class E, int D>
+static hipError_t launch_dkdv(const DenseArgs& a, dim3 g, hipStream_t st) {
+  const int mk = mask_kind(a.mask);
+  if (a.drop.enabled) {
+    if (mk == kArith) return launch((dense_bwd_dkdv_kernel<E, D, kArith, true>), g, dim3(256), 0, st, a);
+    if (mk == kBlock) return launch((dense_bwd_dkdv_kernel<E, D, kBlock, true>), g, dim3(256), 0, st, a);
+    return launch((dense_bwd_dkdv_kernel<E, D, kDenseM, true>), g, dim3(256), 0, st, a);
+  }
+  if (mk == kArith) return launch((dense_bwd_dkdv_kernel<E, D, kArith, false>), g, dim3(256), 0, st, a);
+  if (mk == kBlock) return launch((dense_bwd_dkdv_kernel<E, D, kBlock, false>), g, dim3(256), 0, st, a);
+  return launch((dense_bwd_dkdv_kernel<E, D, kDenseM, false>), g, dim3(256), 0, st, a);
+}
+
+template <class E, int D>
+static hipError_t launch_dq(const DenseArgs& a, dim3 g, hipStream_t st, int n_qtiles) {
+  const int mk = mask_kind(a.mask);
+  if (a.drop.enabled) {
+    if (mk == kArith) return launch((dense_bwd_dq_kernel<E, D, kArith, true>), g, dim3(256), 0, st, a, n_qtiles);
+    if (mk == kBlock) return launch((dense_bwd_dq_kernel<E, D, kBlock, true>), g, dim3(256), 0, st, a, n_qtiles);
+    return launch((dense_bwd_dq_kernel<E, D, kDenseM, true>), g, dim3(256), 0, st, a, n_qtiles);
+  }
+  if (mk == kArith) return launch((dense_bwd_dq_kernel<E, D, kArith, false>), g, dim3(256), 0, st, a, n_qtiles);
+  if (mk == kBlock) return launch((dense_bwd_dq_kernel<E, D, kBlock, false>), g, dim3(256), 0, st, a, n_qtiles);
+  return launch((dense_bwd_dq_kernel<E, D, kDenseM, false>), g, dim3(256), 0, st, a, n_qtiles);
+}
+
+template <class E, int D>
 static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
   hipStream_t st = (hipStream_t)stream;
   if (phases & 1) {
@@ -439,13 +491,8 @@ static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
   dim3 gk(n_kblocks * a.B * a.Hkv);
   const int n_qtiles = (a.nq + 127) / 128;
   dim3 gq(n_qtiles * a.B * a.H);
-  if (a.drop.enabled) {
-    if (phases & 2) ETS_TRY(launch((dense_bwd_dkdv_kernel<E, D, true>), gk, dim3(256), 0, st, a));
-    if (phases & 4) ETS_TRY(launch((dense_bwd_dq_kernel<E, D, true>), gq, dim3(256), 0, st, a, n_qtiles));
-  } else {
-    if (phases & 2) ETS_TRY(launch((dense_bwd_dkdv_kernel<E, D, false>), gk, dim3(256), 0, st, a));
-    if (phases & 4) ETS_TRY(launch((dense_bwd_dq_kernel<E, D, false>), gq, dim3(256), 0, st, a, n_qtiles));
-  }
+  if (phases & 2) ETS_TRY((launch_dkdv<E, D>(a, gk, st)));
+  if (phases & 4) ETS_TRY((launch_dq<E, D>(a, gq, st, n_qtiles)));
   return 0;
 }
 

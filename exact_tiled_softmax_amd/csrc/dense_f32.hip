@@ -41,7 +41,7 @@ __global__ __launch_bounds__(64) void f32_fwd_kernel(const DenseArgs a) {
     float amax = kNegInf;
     bool any = false;
     for (int j = j0; j < j1; ++j) {
-      if (!allowed1(a.mask, i, j, a.nq, nk)) continue;
+      if (!allowed1<kDenseM>(a.mask, i, j, a.nq, nk, true)) continue;
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < DM; ++r)
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64) void f32_fwd_kernel(const DenseArgs a) {
 #pragma unroll
     for (int r = 0; r < DM; ++r) z[r] *= alpha;
     for (int j = j0; j < j1; ++j) {
-      if (!allowed1(a.mask, i, j, a.nq, nk)) continue;
+      if (!allowed1<kDenseM>(a.mask, i, j, a.nq, nk, true)) continue;
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < DM; ++r)
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const DenseArgs a) {
     dq[r] = 0.f;
   }
   for (int j = 0; j < nk; ++j) {
-    if (!allowed1(a.mask, i, j, a.nq, nk)) continue;
+    if (!allowed1<kDenseM>(a.mask, i, j, a.nq, nk, true)) continue;
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int r = 0; r < DM; ++r) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64) void f32_dkdv_kernel(const DenseArgs a) {
     const float* Q = (const float*)a.Q + (size_t)bh * nq * d;
     const float* G = (const float*)a.G + (size_t)bh * nq * dv;
     for (int i = 0; i < nq; ++i) {
-      if (!allowed1(a.mask, i, j, nq, a.nk)) continue;
+      if (!allowed1<kDenseM>(a.mask, i, j, nq, a.nk, true)) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int r = 0; r < DM; ++r) {

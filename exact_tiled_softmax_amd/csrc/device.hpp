@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <tuple>
+#include <type_traits>
+#include <utility>
 
 #include "params.hpp"
 
@@ -163,23 +165,41 @@ __device__ __forceinline__ u32x4 lds_tr8(const char ETS_LDS* base, int r0, int r
 // position 64k + l, so it fetches the logical chunk that the swizzle maps
 // there.  Rows past last_row are read from last_row instead (finite data; the
 // caller masks them), so no access leaves the tensor.  Completion is awaited
-// with wait_vm() before the barrier that publishes the tile.
+// with a vmcnt wait before the barrier that publishes the tile.  The per-lane
+// parts of the addresses are computed once; an issue costs three VALU
+// operations per instruction (row clamp and byte offset from a scalar base).
+template <int ROWS, int W, int NWAVES>
+struct TileCopy {
+  static constexpr int CPR = W / 8;  // 16-byte chunks per row
+  static constexpr int INSTS = ROWS * CPR / 64;
+  static_assert(INSTS % NWAVES == 0 && 64 % CPR == 0, "tile does not split evenly over the waves");
+  static constexpr int PER_WAVE = INSTS / NWAVES;
+  static constexpr int RPI = 64 / CPR;  // rows per instruction
+  int row;                // tile row of this lane in the wave's first instruction
+  int col[PER_WAVE];      // byte offset, within its row, of the chunk this lane fetches
+  int inst0;              // first instruction index of the wave (uniform)
+  __device__ __forceinline__ TileCopy(int wave, int lane) {
+    inst0 = wave * PER_WAVE;
+    row = inst0 * RPI + lane / CPR;
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) col[u] = phys_chunk<2 * W>(row + u * RPI, lane % CPR) * 16;  // involution
+  }
+  // instruction u (0 .. PER_WAVE-1) of the wave's share
+  __device__ __forceinline__ void issue_one(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row,
+                                            int u) const {
+    const unsigned off = (unsigned)min(row0 + row + u * RPI, last_row) * (unsigned)(2 * W) + (unsigned)col[u];
+    __builtin_amdgcn_global_load_lds((const char*)base + off, (void ETS_LDS*)(dst + (inst0 + u) * 1024), 16, 0, 0);
+  }
+  __device__ __forceinline__ void issue(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row) const {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) issue_one(dst, base, row0, last_row, u);
+  }
+};
+
 template <int ROWS, int W, int NWAVES>
 __device__ __forceinline__ void tile_to_lds(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row,
                                             int wave, int lane) {
-  constexpr int CPR = W / 8;
-  constexpr int INSTS = ROWS * CPR / 64;
-  static_assert(INSTS % NWAVES == 0, "tile does not split evenly over the waves");
-  constexpr int PER_WAVE = INSTS / NWAVES;
-#pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u) {
-    const int inst = wave * PER_WAVE + u;
-    const int pos = inst * 64 + lane;
-    const int row = pos / CPR, pc = pos % CPR;
-    const int lc = phys_chunk<2 * W>(row, pc);  // the swizzle is an involution
-    const int grow = min(row0 + row, last_row);
-    __builtin_amdgcn_global_load_lds(base + (size_t)grow * W + lc * 8, (void ETS_LDS*)(dst + inst * 1024), 16, 0, 0);
-  }
+  TileCopy<ROWS, W, NWAVES>(wave, lane).issue(dst, base, row0, last_row);
 }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -285,6 +305,28 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled in the source
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Instruction-scheduler groups (LLVM AMDGPU sched_group_barrier masks): the
+// compiler fills groups in the order they are declared within a basic block.
+enum SchedMask : int { kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100 };
+#define ETS_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+// No instruction may be scheduled across this point.
+#define ETS_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Pins the computation of x before this point (an empty asm that reads x), so
+// that the compiler cannot sink it past a following branch.
+template <class T>
+__device__ __forceinline__ void materialize(const T& x) { asm volatile("" ::"v"(x)); }
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -319,34 +361,45 @@ __device__ __forceinline__ unsigned keep4(const DropArgs& d, int lane_bh, int i,
 }
 
 // ------------------------------------------------------------ allowed sets
-// Allowed bits of keys j0 .. j0+3 for query row i (bit r <-> key j0 + r).
-// check_bm = false skips the block-mask lookup (the caller has established
-// that the block mask allows the whole tile).
-__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk,
-                                             bool check_bm = true) {
-  if (i >= nq) return 0u;
-  unsigned bits = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int j = j0 + r;
-    bool ok = j < nk;
-    if (m.causal) ok = ok && (j <= i);
-    if (m.window > 0) ok = ok && (i - j < m.window);
-    if (check_bm && ok && m.block_mask) ok = m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] != 0;
-    if (ok && m.dense_mask) ok = m.dense_mask[(size_t)i * nk + j] != 0;
-    bits |= (unsigned)ok << r;
-  }
-  return bits;
-}
+// Kernels are compiled per mask kind so that the common causal / window case
+// carries no per-element memory lookups:
+//   kArith  causal and look-back window only (plus ragged tails),
+//   kBlock  + the tile mask, read per element only in tiles where it is mixed,
+//   kDenseM + the dense mask.
+enum MaskKind { kArith = 0, kBlock = 1, kDenseM = 2 };
 
-// Single (row i, key j) test.
-__device__ __forceinline__ bool allowed1(const MaskArgs& m, int i, int j, int nq, int nk, bool check_bm = true) {
+inline int mask_kind(const MaskArgs& m) { return m.dense_mask ? kDenseM : (m.block_mask ? kBlock : kArith); }
+
+// Single (row i, key j) test.  check_bm = false skips the block-mask lookup
+// (the caller has established that the block mask allows the whole tile).
+template <int MK>
+__device__ __forceinline__ bool allowed1(const MaskArgs& m, int i, int j, int nq, int nk, bool check_bm) {
   if (i >= nq || j >= nk) return false;
   if (m.causal && j > i) return false;
   if (m.window > 0 && i - j >= m.window) return false;
-  if (check_bm && m.block_mask && m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] == 0) return false;
-  if (m.dense_mask && m.dense_mask[(size_t)i * nk + j] == 0) return false;
+  if constexpr (MK >= kBlock)
+    if (check_bm && m.block_mask && m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] == 0) return false;
+  if constexpr (MK == kDenseM)
+    if (m.dense_mask && m.dense_mask[(size_t)i * nk + j] == 0) return false;
   return true;
+}
+
+// Allowed bits of keys j0 .. j0+3 for query row i (bit r <-> key j0 + r).
+template <int MK>
+__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk, bool check_bm) {
+  unsigned bits = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bits |= (allowed1<MK>(m, i, j0 + r, nq, nk, check_bm) ? 1u : 0u) << r;
+  return bits;
+}
+
+// Allowed bits of query rows i0 .. i0+3 for key j (bit r <-> row i0 + r).
+template <int MK>
+__device__ __forceinline__ unsigned allowed4_rows(const MaskArgs& m, int i0, int j, int nq, int nk, bool check_bm) {
+  unsigned bits = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bits |= (allowed1<MK>(m, i0 + r, j, nq, nk, check_bm) ? 1u : 0u) << r;
+  return bits;
 }
 
 enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2, kClassMask = 3, kCheckBlockMask = 4 };
@@ -355,6 +408,7 @@ enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2, kClassMask = 3, kCheckBloc
 // jb may run past nk for a ragged last tile).  Uniform across the wave.
 // Returns kEmpty, kFull or kPartial, plus kCheckBlockMask when the block mask
 // is mixed inside the rectangle and must be read per element.
+template <int MK>
 __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int ja, int jb, int nq, int nk) {
   if (ia >= nq || ja >= nk) return kEmpty;
   // rows or keys past the end are present in the tile: mask them per element
@@ -369,7 +423,7 @@ __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int j
     if (ia - jb >= m.window) return kEmpty;
     if (ib - ja >= m.window) cls = kPartial;
   }
-  if (m.block_mask) {
+  if (MK >= kBlock && m.block_mask) {
     const int r0 = ia / m.bq, r1 = ib / m.bq, c0 = ja / m.bk, c1 = jb / m.bk;
     if ((r1 - r0 + 1) * (c1 - c0 + 1) > 64) {
       cls = kPartial | kCheckBlockMask;
@@ -384,7 +438,7 @@ __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int j
       if (ones != tot) cls = kPartial | kCheckBlockMask;
     }
   }
-  if (m.dense_mask) cls = (cls & kCheckBlockMask) | kPartial;
+  if (MK == kDenseM && m.dense_mask) cls = (cls & kCheckBlockMask) | kPartial;
   return cls;
 }
 

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
   char ETS_LDS* smem = (char ETS_LDS*)smem_dyn;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int G = lane >> 4, l16 = lane & 15;
   const int t = blockIdx.x;
   const int head = 16 * wave + l16;
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
   extern __shared__ __attribute__((aligned(16))) char smem_dyn[];
   char ETS_LDS* smem = (char ETS_LDS*)smem_dyn;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int G = lane >> 4, l16 = lane & 15;
   const int t = blockIdx.x;
   const int head = 16 * wave + l16;
@@ -366,7 +368,8 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
   char ETS_LDS* pbuf = smem + 2 * TILEB;  // P  [key][head]
   char ETS_LDS* dbuf = pbuf + PB;         // dS [key][head]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int G = lane >> 4, l16 = lane & 15;
   const int t = blockIdx.x;
   const int head = 16 * wave + l16;
