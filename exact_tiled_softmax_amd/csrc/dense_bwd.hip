@@ -75,204 +75,390 @@ __device__ __forceinline__ unsigned keep4_rows(const DropArgs& d, int lane_bh, i
 }
 
 // --------------------------------------------------------------------- dK, dV
+// Group plans of a step with NMQ query blocks: group gi is A (S, dP) or B
+// (dV, dK) of block mq[gi]; W(wq[gi]) runs under group gi, the LSE / D rows
+// of W(nwq[gi]) are read at its end, and the copies of the next step are
+// spread over the groups marked in `copies`.
+template <int NMQ>
+struct DkPlan;
+template <>
+struct DkPlan<2> {  // A0 | A1+W0 | B0+W1 | B1
+  static constexpr int NG = 4;
+  static constexpr bool isA[4] = {true, true, false, false};
+  static constexpr int mq[4] = {0, 1, 0, 1};
+  static constexpr int wq[4] = {-1, 0, 1, -1};
+  static constexpr int nwq[4] = {0, 1, -1, -1};
+  static constexpr bool copies[4] = {true, false, false, false};
+};
+template <>
+struct DkPlan<4> {  // A0 | A1+W0 | B0 | A2+W1 | B1 | A3+W2 | B2+W3 | B3
+  static constexpr int NG = 8;
+  static constexpr bool isA[8] = {true, true, false, true, false, true, false, false};
+  static constexpr int mq[8] = {0, 1, 0, 2, 1, 3, 2, 3};
+  static constexpr int wq[8] = {-1, 0, -1, 1, -1, 2, 3, -1};
+  static constexpr int nwq[8] = {0, -1, 1, -1, 2, 3, -1, -1};
+  static constexpr bool copies[8] = {true, false, true, false, false, false, false, false};
+};
+template <class P>
+constexpr int plan_start(int gi, int na, int nb) {
+  int s0 = 0;
+  for (int k = 0; k < gi; ++k) s0 += P::isA[k] ? na : nb;
+  return s0;
+}
+template <class P>
+constexpr int plan_group(int t, int na, int nb) {
+  int gi = 0;
+  while (gi + 1 < P::NG && t >= plan_start<P>(gi + 1, na, nb)) ++gi;
+  return gi;
+}
+template <class P>
+constexpr int plan_copy_groups() {
+  int n = 0;
+  for (int k = 0; k < P::NG; ++k) n += P::copies[k] ? 1 : 0;
+  return n;
+}
+template <class P>
+constexpr int plan_copy_rank(int gi) {  // index of group gi among the copy groups
+  int n = 0;
+  for (int k = 0; k < gi; ++k) n += P::copies[k] ? 1 : 0;
+  return n;
+}
+
+// A workgroup owns 128 keys (32 per wave) of one K/V head; a step is one
+// query head of the group and a tile of BQ = 64 query rows, blocks mq of 32
+// rows.  Per block a wave runs
+//   A(mq): S = Q K^T and dP = G V^T            (2 D/16 MFMAs)
+//   W(mq): P and gamma from S, dP, LSE, D       (VALU)
+//   B(mq): dV^T += G^T P~, dK^T += Q^T gamma   (4 D/32 MFMAs)
+// in a fixed order (DkPlan), one MFMA per slot with operands read three slots
+// ahead, so the VALU work of a block runs under the MFMAs of another; the
+// copy of the next step's rows into the other LDS stage is spread over the
+// first group.
 template <class E, int D, int MK, bool DROP>
-__global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs a) {
-  constexpr int BQ = 64;             // query rows per tile
+__global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs a, int n_kblocks) {
+  constexpr int BQ = 64;  // query rows per step
+  typedef DkPlan<BQ / 32> Plan;
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BQ * ROWB;
-  constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q, G tiles + LSE2, D
+  constexpr int NA = 2 * KS, NB = 4 * MD;  // slots of A(mq), B(mq)
   typedef typename E::vec8 vec8;
+  typedef std::integral_constant<int, 0> Stage0;
+  typedef std::integral_constant<int, 1> Stage1;
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB];
-  char ETS_LDS* smem = (char ETS_LDS*)smem_raw;
+  // one array per (stage, tensor): reads of one stage never wait for the
+  // copies into the other.  L: LSE2 (128 floats) then D (128 floats).
+  __shared__ __attribute__((aligned(16))) char ldsQ0[TILEB], ldsG0[TILEB], ldsQ1[TILEB], ldsG1[TILEB];
+  __shared__ __attribute__((aligned(16))) char ldsL0[1024], ldsL1[1024];
+  auto qbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsQ0;
+    else return (char ETS_LDS*)ldsQ1;
+  };
+  auto gbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsG0;
+    else return (char ETS_LDS*)ldsG1;
+  };
+  auto lbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsL0;
+    else return (char ETS_LDS*)ldsL1;
+  };
+  // LSE2 and D rows through one buffer resource: the workspace holds D
+  // first and the base-2 LSE after it, each with 64 padding rows
+  const uint32_t lse_off = (uint32_t)((const char*)a.Lws - (const char*)a.Dws);
+  const __amdgpu_buffer_rsrc_t Wrs = make_rsrc(a.Dws, lse_off + (uint32_t)((a.B * a.H * a.nq + 64) * 4));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h32 = lane >> 5, l32 = lane & 31;
   const int nq = a.nq, nk = a.nk;
-  const int BG = a.B * a.Hkv;
-  const int kb = (int)(blockIdx.x / BG), bg = (int)(blockIdx.x % BG);  // key block (heavy first), (batch, kv head)
-  const int b = bg / a.Hkv, g = bg % a.Hkv, grp = a.H / a.Hkv;
-  const int k0 = kb * 128, kw0 = k0 + 32 * wave;
-  const int key = kw0 + l32;
-
-  const uint16_t* Kp = (const uint16_t*)a.K + (size_t)bg * nk * D;
-  const uint16_t* Vp = (const uint16_t*)a.V + (size_t)bg * nk * D;
-
-  // this wave's 32 keys as B operands of S = Q K^T and dP = G V^T
-  vec8 kreg[KS], vreg[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
-    if (key < nk) {
-      kv = *(const u32x4*)(Kp + (size_t)key * D + 16 * kk + 8 * h32);
-      vv = *(const u32x4*)(Vp + (size_t)key * D + 16 * kk + 8 * h32);
-    }
-    kreg[kk] = as_vec8<E>(kv);
-    vreg[kk] = as_vec8<E>(vv);
-  }
-
-  f32x16 dk[MD], dv[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[md][r] = 0.f; dv[md][r] = 0.f; }
-
-  // query-tile range that can see keys [k0, k0 + 127]
-  const int klast = min(k0 + 127, nk - 1);
-  int qt_lo = 0, qt_hi = (nq - 1) / BQ;
-  if (a.mask.causal) qt_lo = k0 / BQ;
-  if (a.mask.window > 0) qt_hi = min(qt_hi, (klast + a.mask.window - 1) / BQ);
-  const int n_qt = qt_hi - qt_lo + 1;
-  const int total = (n_qt > 0) ? n_qt * grp : 0;  // (head, q-tile) steps
-
-  auto wg_nonempty = [&](int step) {
-    const int qt = qt_lo + step % n_qt;
-    return classify<MK>(a.mask, qt * BQ, qt * BQ + BQ - 1, k0, k0 + 127, nq, nk) != kEmpty;
-  };
-  auto next_step = [&](int s) {
-    for (++s; s < total; ++s)
-      if (wg_nonempty(s)) return s;
-    return -1;
-  };
-  // Q and G tiles straight to LDS; LSE2 and D (64 floats each) by one
-  // half-wave instruction (the workspace holds 64 padding rows after the last)
-  auto load = [&](int s, int st) {
-    const int h = g * grp + s / n_qt, qt = qt_lo + s % n_qt;
-    const size_t lane_off = (size_t)(b * a.H + h) * nq;
-    char ETS_LDS* qt_ = smem + st * STAGEB;
-    tile_to_lds<BQ, D, 4>(qt_, (const uint16_t*)a.Q + lane_off * D, qt * BQ, nq - 1, wave, lane);
-    tile_to_lds<BQ, D, 4>(qt_ + TILEB, (const uint16_t*)a.G + lane_off * D, qt * BQ, nq - 1, wave, lane);
-    if (wave == 0 && lane < 32) {
-      const float* src = (lane < 16 ? a.Lws : a.Dws) + lane_off + qt * BQ + 4 * (lane & 15);
-      __builtin_amdgcn_global_load_lds(src, (void ETS_LDS*)(qt_ + 2 * TILEB), 16, 0, 0);
-    }
-  };
-
-  int s = (total > 0) ? (wg_nonempty(0) ? 0 : next_step(0)) : -1;
-  int st = 0;
-  if (s >= 0) load(s, 0);
-  wait_vm();
-  __syncthreads();
+  const int BG = a.B * a.Hkv, grp = a.H / a.Hkv;
   const float sl2 = a.scale_log2;
   const RowOps32<ROWB> rops(lane);
   const TrOps32<ROWB> tops(lane);
+  const TileCopy<BQ, D, 4> tcopy(wave, lane);
+  constexpr int PW = TileCopy<BQ, D, 4>::PER_WAVE;
+  constexpr int NCOPY = 2 * PW;  // Q and G copy instructions per wave per step
 
-  while (s >= 0) {
-    const int nxt = next_step(s);
-    if (nxt >= 0) load(nxt, st ^ 1);
-    const int h = g * grp + s / n_qt, qt = qt_lo + s % n_qt, qb0 = qt * BQ;
-    const int lane_bh = b * a.H + h;
-    const char ETS_LDS* qt_ = smem + st * STAGEB;
-    const char ETS_LDS* gt_ = qt_ + TILEB;
-    const float ETS_LDS* ls = (const float ETS_LDS*)(gt_ + TILEB);
-    const float ETS_LDS* ds = ls + BQ;
-    const int cinfo = classify<MK>(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nq, nk);
-    const int cls = cinfo & kClassMask;
-    const bool cbm = (cinfo & kCheckBlockMask) != 0;
+  // Persistent workgroups: workgroup w of G takes items w, 2G-1-w, 2G+w, ...
+  // of the list (key block, (batch, kv head)), key blocks with the most
+  // query tiles first.
+  const int G = (int)gridDim.x, n_items = n_kblocks * BG;
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (item >= n_items) continue;
+    const int kb = item / BG, bg = item % BG;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int k0 = kb * 128, kw0 = k0 + 32 * wave;
+    const int key = kw0 + l32;  // this lane's key
 
-    if (cls != kEmpty) {
+    const uint16_t* Kp = (const uint16_t*)a.K + (size_t)bg * nk * D;
+    const uint16_t* Vp = (const uint16_t*)a.V + (size_t)bg * nk * D;
+
+    // this wave's 32 keys as B operands of S = Q K^T and dP = G V^T
+    vec8 kreg[KS], vreg[KS];
 #pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {  // 32 query rows at a time
-        f32x16 sc, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
-        // Q and G operands read one k-step ahead of their MFMAs
-        vec8 qa[2], ga[2];
-        qa[0] = as_vec8<E>(lds_b128(qt_, rops.off(32 * mq, 0)));
-        ga[0] = as_vec8<E>(lds_b128(gt_, rops.off(32 * mq, 0)));
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          if (kk + 1 < KS) {
-            qa[(kk + 1) & 1] = as_vec8<E>(lds_b128(qt_, rops.off(32 * mq, kk + 1)));
-            ga[(kk + 1) & 1] = as_vec8<E>(lds_b128(gt_, rops.off(32 * mq, kk + 1)));
-          }
-          sc = E::mfma32(qa[kk & 1], kreg[kk], sc);
-          dp = E::mfma32(ga[kk & 1], vreg[kk], dp);
-        }
-        // S and dP: lane = key, entries r = query rows 32mq + 8(r/4) + 4h32 + r%4
-        uint32_t pw[8], gw[8];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qr = 32 * mq + 8 * g4 + 4 * h32;  // first of 4 query rows in the tile
-          const f32x4 l4 = *(const f32x4 ETS_LDS*)(ls + qr);
-          const f32x4 d4 = *(const f32x4 ETS_LDS*)(ds + qr);
-          unsigned allow = 0xFu, keep = 0xFu;
-          if (cls == kPartial) allow = allowed4_rows<MK>(a.mask, qb0 + qr, key, nq, nk, cbm);
-          if constexpr (DROP) keep = keep4_rows(a.drop, lane_bh, qb0 + qr, key);
-          float pk[4], gm[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = fast_exp2(fmaf(sc[4 * g4 + r], sl2, -l4[r]));
-            float dpv = dp[4 * g4 + r];
-            bool kp = true;
-            if constexpr (DROP) {
-              kp = (keep >> r) & 1u;
-              dpv = kp ? dpv * a.drop.inv_keep : 0.f;
-            }
-            const bool al = (allow >> r) & 1u;
-            pk[r] = (al && kp) ? pv : 0.f;
-            gm[r] = al ? pv * (dpv - d4[r]) : 0.f;
-          }
-          pw[2 * g4] = E::pack2(pk[0], pk[1]);
-          pw[2 * g4 + 1] = E::pack2(pk[2], pk[3]);
-          gw[2 * g4] = E::pack2(gm[0], gm[1]);
-          gw[2 * g4 + 1] = E::pack2(gm[2], gm[3]);
-        }
-        // dV^T += G^T P~, dK^T += Q^T gamma over these 32 queries (2 k-steps);
-        // transpose operands read one step ahead
-        vec8 pb[2], gb[2];
-#pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int o = 4 * kk2;
-          pb[kk2] = as_vec8<E>(u32x4{pw[o], pw[o + 1], pw[o + 2], pw[o + 3]});
-          gb[kk2] = as_vec8<E>(u32x4{gw[o], gw[o + 1], gw[o + 2], gw[o + 3]});
-        }
-        constexpr int NT = 2 * MD;
-        vec8 gta[2], qta[2];
-        gta[0] = as_vec8<E>(tops.read(gt_, 32 * mq, 0));
-        qta[0] = as_vec8<E>(tops.read(qt_, 32 * mq, 0));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int kk2 = t / MD, md = t % MD;
-          if (t + 1 < NT) {
-            const int R1 = 32 * mq + 16 * ((t + 1) / MD), md1 = (t + 1) % MD;
-            gta[(t + 1) & 1] = as_vec8<E>(tops.read(gt_, R1, md1));
-            qta[(t + 1) & 1] = as_vec8<E>(tops.read(qt_, R1, md1));
-          }
-          dv[md] = E::mfma32(gta[t & 1], pb[kk2], dv[md]);
-          dk[md] = E::mfma32(qta[t & 1], gb[kk2], dk[md]);
-        }
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+      if (key < nk) {
+        kv = *(const u32x4*)(Kp + (size_t)key * D + 16 * kk + 8 * h32);
+        vv = *(const u32x4*)(Vp + (size_t)key * D + 16 * kk + 8 * h32);
       }
+      kreg[kk] = as_vec8<E>(kv);
+      vreg[kk] = as_vec8<E>(vv);
     }
-
-    wait_vm();
-    __syncthreads();
-    st ^= 1;
-    s = nxt;
-  }
-
-  // ---- epilogue: dK = c dK^T, dV = (1/(1-rho)) dV^T; lane holds one key
-  if (key < nk) {
-    uint16_t* dKp = (uint16_t*)a.dK + (size_t)bg * nk * D + (size_t)key * D;
-    uint16_t* dVp = (uint16_t*)a.dV + (size_t)bg * nk * D + (size_t)key * D;
-    const float ck = a.scale;
-    const float cv = DROP ? a.drop.inv_keep : 1.f;
+    f32x16 dk[MD], dv[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int col = 32 * md + 8 * g4 + 4 * h32;
-        u32x2 wk, wv;
-        wk[0] = E::pack2(dk[md][4 * g4] * ck, dk[md][4 * g4 + 1] * ck);
-        wk[1] = E::pack2(dk[md][4 * g4 + 2] * ck, dk[md][4 * g4 + 3] * ck);
-        wv[0] = E::pack2(dv[md][4 * g4] * cv, dv[md][4 * g4 + 1] * cv);
-        wv[1] = E::pack2(dv[md][4 * g4 + 2] * cv, dv[md][4 * g4 + 3] * cv);
-        *(u32x2*)(dKp + col) = wk;
-        *(u32x2*)(dVp + col) = wv;
+      for (int r2 = 0; r2 < 16; ++r2) { dk[md][r2] = 0.f; dv[md][r2] = 0.f; }
+
+    // steps s = (head in group) * n_qt + (query tile - qt_lo)
+    const int klast = min(k0 + 127, nk - 1);
+    int qt_lo = 0, qt_hi = (nq - 1) / BQ;
+    if (a.mask.causal) qt_lo = k0 / BQ;
+    if (a.mask.window > 0) qt_hi = min(qt_hi, (klast + a.mask.window - 1) / BQ);
+    const int n_qt = qt_hi - qt_lo + 1;
+    const int total = (n_qt > 0) ? n_qt * grp : 0;
+    auto wg_nonempty = [&](int st) {
+      const int qt = qt_lo + st % n_qt;
+      return classify<MK>(a.mask, qt * BQ, qt * BQ + BQ - 1, k0, k0 + 127, nq, nk) != kEmpty;
+    };
+    auto next_of = [&](int st) {
+      for (++st; st < total; ++st)
+        if (MK == kArith || wg_nonempty(st)) return st;
+      return -1;
+    };
+    auto step_rows = [&](int st, size_t& lane_off, int& qb0) __attribute__((always_inline)) {
+      const int h = g * grp + st / n_qt;
+      lane_off = (size_t)(b * a.H + h) * nq;
+      qb0 = (qt_lo + st % n_qt) * BQ;
+    };
+    // copy instruction u of step st into stage `stg`: Q rows, then G rows
+    auto copy_one = [&](int st, auto stg, int u) __attribute__((always_inline)) {
+      size_t lo;
+      int qb0;
+      step_rows(st, lo, qb0);
+      const uint32_t lane_bytes = (uint32_t)nq * D * 2;
+      if (u < PW) tcopy.issue_one(qbuf(stg), make_rsrc((const uint16_t*)a.Q + lo * D, lane_bytes), qb0, nq - 1, u);
+      else tcopy.issue_one(gbuf(stg), make_rsrc((const uint16_t*)a.G + lo * D, lane_bytes), qb0, nq - 1, u - PW);
+    };
+    // LSE2 and D rows qb0 .. qb0+127 of step st (wave 0): lanes 0-31 LSE2 to
+    // bytes 0-511, lanes 32-63 D to bytes 512-1023 (rows past the workspace
+    // read as zero through the resource bound)
+    auto copy_lse = [&](int st, auto stg) __attribute__((always_inline)) {
+      if (wave == 0) {
+        size_t lo;
+        int qb0;
+        step_rows(st, lo, qb0);
+        const uint32_t off = (uint32_t)((lo + qb0 + 4 * l32) * 4) + (h32 ? 0u : lse_off);
+        copy16_to_lds(Wrs, off, (void ETS_LDS*)lbuf(stg));
       }
+    };
+
+    // MFMA operands in slot order (groups as in the plan); A slots alternate
+    // Q and G rows per k-step, B slots alternate G^T (dV) and Q^T (dK) per
+    // (kh, md).
+    constexpr int NSLOT = (BQ / 32) * (NA + NB);
+    auto operand = [&](auto stg, int t) __attribute__((always_inline)) {
+      const int gi = plan_group<Plan>(t, NA, NB);
+      const int u = t - plan_start<Plan>(gi, NA, NB), mq = Plan::mq[gi];
+      if (Plan::isA[gi]) {
+        const int kk = u / 2;
+        return as_vec8<E>(lds_b128((u & 1) ? gbuf(stg) : qbuf(stg), rops.off(32 * mq, kk)));
+      }
+      const int kh = u / (2 * MD), md = (u % (2 * MD)) / 2;
+      return as_vec8<E>(tops.read((u & 1) ? qbuf(stg) : gbuf(stg), 32 * mq + 16 * kh, md));
+    };
+
+    // rows interval of this lane's key for arithmetic masks: query row
+    // base + c is allowed iff (unsigned)(c - lo) <= rng
+    auto arith_interval = [&](int base, int& lo, unsigned& rng) __attribute__((always_inline)) {
+      int ilo = 0, ihi = nq - 1;
+      if (a.mask.causal) ilo = max(ilo, key);
+      if (a.mask.window > 0) ihi = min(ihi, key + a.mask.window - 1);
+      const bool any = key < nk && ilo <= ihi;
+      lo = any ? ilo - base : (1 << 24);
+      rng = any ? (unsigned)(ihi - ilo) : 0u;
+    };
+    // P and gamma of one block: rows 32mq + 8g4 + 4h32 + r2 (this lane's key)
+    struct Weights {
+      uint32_t pw[8], gw[8];
+      f32x4 l4[4], d4[4];
+      unsigned allow[4], keep[4];
+    };
+    auto read_ld = [&](Weights& w, auto stg, int mq) __attribute__((always_inline)) {
+      const float ETS_LDS* ls = (const float ETS_LDS*)lbuf(stg);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qr = 32 * mq + 8 * g4 + 4 * h32;
+        w.l4[g4] = *(const f32x4 ETS_LDS*)(ls + qr);
+        w.d4[g4] = *(const f32x4 ETS_LDS*)(ls + 128 + qr);  // D after 128 LSE2 floats
+      }
+    };
+    // sub-part k = 2 g4 + half: rows r2 = 2 half, 2 half + 1 of group g4
+    auto weights = [&](Weights& w, const f32x16& sc, const f32x16& dp, int k, int mq, int qb0, int lane_bh,
+                       auto part_tag, bool cbm) __attribute__((always_inline)) {
+      constexpr bool PART = decltype(part_tag)::value;
+      const int g4 = k / 2, half = k % 2;
+      const int qr = 32 * mq + 8 * g4 + 4 * h32;
+      if (half == 0) {
+        w.allow[g4] = 0xFu;
+        w.keep[g4] = 0xFu;
+        if constexpr (PART) {
+          if constexpr (MK == kArith) {
+            int lo;
+            unsigned rng;
+            arith_interval(qb0 + qr, lo, rng);
+            unsigned al = 0;
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) al |= ((unsigned)(r2 - lo) <= rng ? 1u : 0u) << r2;
+            w.allow[g4] = al;
+          } else {
+            w.allow[g4] = allowed4_rows<MK>(a.mask, qb0 + qr, key, nq, nk, cbm);
+          }
+        }
+        if constexpr (DROP) w.keep[g4] = keep4_rows(a.drop, lane_bh, qb0 + qr, key);
+      }
+      float pk[2], gm[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r2 = 2 * half + e;
+        const float pv = fast_exp2(fmaf(sc[4 * g4 + r2], sl2, -w.l4[g4][r2]));
+        float dpv = dp[4 * g4 + r2];
+        bool kp = true;
+        if constexpr (DROP) {
+          kp = (w.keep[g4] >> r2) & 1u;
+          dpv = kp ? dpv * a.drop.inv_keep : 0.f;
+        }
+        const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
+        pk[e] = (al && kp) ? pv : 0.f;
+        gm[e] = al ? pv * (dpv - w.d4[g4][r2]) : 0.f;
+      }
+      w.pw[2 * g4 + half] = E::pack2(pk[0], pk[1]);
+      w.gw[2 * g4 + half] = E::pack2(gm[0], gm[1]);
+      materialize(w.pw[2 * g4 + half]);
+      materialize(w.gw[2 * g4 + half]);
+    };
+    auto pack_op = [&](const uint32_t (&x)[8], int kh) __attribute__((always_inline)) {
+      return as_vec8<E>(u32x4{x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]});
+    };
+
+    // one step on stage stg; its successor's rows go into the other stage
+    auto step = [&](auto stg, int st, int sn, auto part_tag, bool cbm) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(stg)::value> Next;
+      size_t lo;
+      int qb0;
+      step_rows(st, lo, qb0);
+      const int lane_bh = (int)(lo / nq);
+      copy_lse(sn, Next{});
+      f32x16 sc[BQ / 32], dp[BQ / 32];
+      Weights w[BQ / 32];
+      vec8 opb[4];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) opb[k] = operand(stg, k);
+      static_for<NSLOT>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int gi = plan_group<Plan>(t, NA, NB);
+        constexpr int u = t - plan_start<Plan>(gi, NA, NB);
+        constexpr bool isA = Plan::isA[gi];
+        constexpr int mq = Plan::mq[gi];
+        constexpr int gsz = isA ? NA : NB;
+        if constexpr (t + 3 < NSLOT) opb[(t + 3) % 4] = operand(stg, t + 3);
+        const vec8 op = opb[t % 4];
+        if constexpr (isA) {
+          constexpr int kk = u / 2;
+          if constexpr (u == 0) {
+#pragma unroll
+            for (int r2 = 0; r2 < 16; ++r2) { sc[mq][r2] = 0.f; dp[mq][r2] = 0.f; }
+          }
+          if constexpr (u & 1) dp[mq] = E::mfma32(op, vreg[kk], dp[mq]);
+          else sc[mq] = E::mfma32(op, kreg[kk], sc[mq]);
+        } else {
+          constexpr int kh = u / (2 * MD), md = (u % (2 * MD)) / 2;
+          if constexpr (u & 1) dk[md] = E::mfma32(op, pack_op(w[mq].gw, kh), dk[md]);
+          else dv[md] = E::mfma32(op, pack_op(w[mq].pw, kh), dv[md]);
+        }
+        // copies of the next step in the plan's copy groups
+        if constexpr (Plan::copies[gi]) {
+          constexpr int NCG = plan_copy_groups<Plan>(), per = NCOPY / NCG;
+          constexpr int base = plan_copy_rank<Plan>(gi) * per;
+          static_for<per>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int cu = decltype(uc)::value;
+            if constexpr ((cu * gsz) / per == u) copy_one(sn, Next{}, base + cu);
+          });
+        }
+        // W(wq) runs under group gi; the LSE / D rows of W(nwq) are read at
+        // the end of group gi
+        constexpr int wq = Plan::wq[gi];
+        constexpr int nwq = Plan::nwq[gi];
+        if constexpr (nwq >= 0 && u == gsz - 2) read_ld(w[nwq], stg, nwq);
+        if constexpr (wq >= 0) {
+          static_for<8>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            if constexpr ((k * gsz) / 8 == u) weights(w[wq], sc[wq], dp[wq], k, wq, qb0, lane_bh, part_tag, cbm);
+          });
+        }
+        ETS_FENCE();
+      });
+    };
+    auto empty_step = [&](auto stg, int sn) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(stg)::value> Next;
+      copy_lse(sn, Next{});
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(sn, Next{}, u);
+    };
+    auto finish = [&]() __attribute__((always_inline)) {
+      wait_vm();
+      __syncthreads();
+    };
+    auto general_step = [&](auto stg, int st, int sn) __attribute__((always_inline)) {
+      size_t lo;
+      int qb0;
+      step_rows(st, lo, qb0);
+      const int cinfo = classify<MK>(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nq, nk);
+      const int cls = cinfo & kClassMask;
+      if (cls == kFull) step(stg, st, sn, std::false_type{}, false);
+      else if (cls == kPartial) step(stg, st, sn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      else empty_step(stg, sn);
+      finish();
+    };
+
+    int st = -1;
+    if (total > 0) st = (MK == kArith || wg_nonempty(0)) ? 0 : next_of(0);
+    if (st >= 0) {
+      copy_lse(st, Stage0{});
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(st, Stage0{}, u);
+    }
+    finish();
+    for (int p = 0; st >= 0; ++p) {
+      const int sn = next_of(st);
+      if (p & 1) general_step(Stage1{}, st, sn >= 0 ? sn : st);
+      else general_step(Stage0{}, st, sn >= 0 ? sn : st);
+      st = sn;
+    }
+
+    // ---- epilogue: dK = c dK^T, dV = (1/(1-rho)) dV^T; lane holds one key
+    if (key < nk) {
+      uint16_t* dKp = (uint16_t*)a.dK + (size_t)bg * nk * D + (size_t)key * D;
+      uint16_t* dVp = (uint16_t*)a.dV + (size_t)bg * nk * D + (size_t)key * D;
+      const float ck = a.scale;
+      const float cv = DROP ? a.drop.inv_keep : 1.f;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * md + 8 * g4 + 4 * h32;
+          u32x2 wk, wv;
+          wk[0] = E::pack2(dk[md][4 * g4] * ck, dk[md][4 * g4 + 1] * ck);
+          wk[1] = E::pack2(dk[md][4 * g4 + 2] * ck, dk[md][4 * g4 + 3] * ck);
+          wv[0] = E::pack2(dv[md][4 * g4] * cv, dv[md][4 * g4 + 1] * cv);
+          wv[1] = E::pack2(dv[md][4 * g4 + 2] * cv, dv[md][4 * g4 + 3] * cv);
+          *(u32x2*)(dKp + col) = wk;
+          *(u32x2*)(dVp + col) = wv;
+        }
+    }
   }
 }
 
@@ -340,10 +526,13 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
     return -1;
   };
 
+  const TileCopy<BK, D, 4> tcopy(wave, lane);
+  const __amdgpu_buffer_rsrc_t Krs = make_rsrc(Kp, (uint32_t)nk * D * 2);
+  const __amdgpu_buffer_rsrc_t Vrs = make_rsrc(Vp, (uint32_t)nk * D * 2);
   auto load = [&](int jt, int stage) {
     char ETS_LDS* kt = smem + stage * 2 * TILEB;
-    tile_to_lds<BK, D, 4>(kt, Kp, jt * BK, nk - 1, wave, lane);
-    tile_to_lds<BK, D, 4>(kt + TILEB, Vp, jt * BK, nk - 1, wave, lane);
+    tcopy.issue(kt, Krs, jt * BK, nk - 1);
+    tcopy.issue(kt + TILEB, Vrs, jt * BK, nk - 1);
   };
 
   int jt = (jt_lo <= jt_hi && wg_nonempty(jt_lo)) ? jt_lo : next_tile(jt_lo);
@@ -453,17 +642,28 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a,
   }
 }
 
+template <class E, int D, int MK, bool DROP>
+static int launch_dkdv_k(const DenseArgs& a, hipStream_t st) {
+  const int n_kblocks = (a.nk + 127) / 128;
+  const int n_items = n_kblocks * a.B * a.Hkv;
+  int slots = 0;
+  ETS_TRY(resident_slots(dense_bwd_dkdv_kernel<E, D, MK, DROP>, 256, &slots));
+  ETS_TRY(launch((dense_bwd_dkdv_kernel<E, D, MK, DROP>), dim3(min(n_items, slots)), dim3(256), 0, st, a,
+                 n_kblocks));
+  return 0;
+}
+
 template <class E, int D>
-static hipError_t launch_dkdv(const DenseArgs& a, dim3 g, hipStream_t st) {
+static int launch_dkdv(const DenseArgs& a, hipStream_t st) {
   const int mk = mask_kind(a.mask);
   if (a.drop.enabled) {
-    if (mk == kArith) return launch((dense_bwd_dkdv_kernel<E, D, kArith, true>), g, dim3(256), 0, st, a);
-    if (mk == kBlock) return launch((dense_bwd_dkdv_kernel<E, D, kBlock, true>), g, dim3(256), 0, st, a);
-    return launch((dense_bwd_dkdv_kernel<E, D, kDenseM, true>), g, dim3(256), 0, st, a);
+    if (mk == kArith) return launch_dkdv_k<E, D, kArith, true>(a, st);
+    if (mk == kBlock) return launch_dkdv_k<E, D, kBlock, true>(a, st);
+    return launch_dkdv_k<E, D, kDenseM, true>(a, st);
   }
-  if (mk == kArith) return launch((dense_bwd_dkdv_kernel<E, D, kArith, false>), g, dim3(256), 0, st, a);
-  if (mk == kBlock) return launch((dense_bwd_dkdv_kernel<E, D, kBlock, false>), g, dim3(256), 0, st, a);
-  return launch((dense_bwd_dkdv_kernel<E, D, kDenseM, false>), g, dim3(256), 0, st, a);
+  if (mk == kArith) return launch_dkdv_k<E, D, kArith, false>(a, st);
+  if (mk == kBlock) return launch_dkdv_k<E, D, kBlock, false>(a, st);
+  return launch_dkdv_k<E, D, kDenseM, false>(a, st);
 }
 
 template <class E, int D>
@@ -487,11 +687,12 @@ static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
     const int prep_threads = (rows + 64) * (D / 8);
     ETS_TRY(launch((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows));
   }
-  const int n_kblocks = (a.nk + 127) / 128;
-  dim3 gk(n_kblocks * a.B * a.Hkv);
   const int n_qtiles = (a.nq + 127) / 128;
   dim3 gq(n_qtiles * a.B * a.H);
-  if (phases & 2) ETS_TRY((launch_dkdv<E, D>(a, gk, st)));
+  if (phases & 2) {
+    const int rc = launch_dkdv<E, D>(a, st);
+    if (rc) return rc;
+  }
   if (phases & 4) ETS_TRY((launch_dq<E, D>(a, gq, st, n_qtiles)));
   return 0;
 }

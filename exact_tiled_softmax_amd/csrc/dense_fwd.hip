@@ -14,7 +14,7 @@
 //     rows), so a query's running max and sum live in one lane plus its
 //     partner lane l ^ 32;
 //   * K and V tiles of 64 keys go straight from HBM into a two-stage LDS ring
-//     (global_load_lds, swizzled rows); the copy of the next tile is issued
+//     (buffer_load ... lds, swizzled rows); the copy of the next tile is issued
 //     while the current one is used.  The PV product is accumulated
 //     transposed, O^T += V^T P^T, with V^T read by ds_read_b64_tr_b16 and P^T
 //     fed straight from the S^T accumulators (no shuffles);
@@ -22,10 +22,10 @@
 //     online-summary step, in the order
 //       S(0) | S(1) + summary(0) | PV(0) + summary(1) | PV(1)
 //     so that the VALU work of one block (max, exponentials, packing) is
-//     issued between the MFMAs of the other.  For tiles that every row of the
-//     workgroup sees whole (the bulk of a causal or windowed pass) this order
-//     is fixed by hand, one MFMA per slot with its operand reads two slots
-//     ahead; masked tiles take a general path;
+//     issued between the MFMAs of the other.  The order is fixed by hand,
+//     one MFMA per slot with its operand reads two slots ahead; tiles that a
+//     wave's rows see only in part apply the mask in the same slots (for
+//     causal and window masks as one key interval per row);
 //   * scores are kept in base 2 (c*log2 e folded into one FMA before
 //     v_exp_f32); the reference maximum of a row is only raised when a block's
 //     maximum exceeds it by more than kRescaleSlack (log2 units), which keeps
@@ -67,368 +67,357 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void dense_fwd_kernel(con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h32 = lane >> 5, l32 = lane & 31;
 
-  // heaviest query tiles first; consecutive blocks walk (batch, head) so a
-  // lane's tiles stay on one XCD when B*H is a multiple of 8
-  const int BH = a.B * a.H;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
-  const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
-  const int nq = a.nq, nk = a.nk;
-  const int q0 = qt * BQ, qw0 = q0 + wave * 32;
-  const int qi = qw0 + l32;  // this lane's query row
+  // Persistent workgroups: workgroup w of G takes items w, 2G-1-w, 2G+w, ...
+  // (boustrophedon over the heaviest-first list), which balances the causal
+  // triangle without atomics and keeps every slot busy until the end.
+  const int G = (int)gridDim.x, n_items = n_qtiles * a.B * a.H;
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (item >= n_items) continue;
+    // work item = one query tile of one (batch, head); items are numbered
+    // heaviest first and consecutive items walk (batch, head)
+    const int BH = a.B * a.H;
+    const int qt = n_qtiles - 1 - item / BH;
+    const int bh = item % BH;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
+    const int nq = a.nq, nk = a.nk;
+    const int q0 = qt * BQ, qw0 = q0 + wave * 32;
+    const int qi = qw0 + l32;  // this lane's query row
 
-  const uint16_t* Qp = (const uint16_t*)a.Q + (size_t)bh * nq * D;
-  const uint16_t* Kp = (const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D;
-  const uint16_t* Vp = (const uint16_t*)a.V + (size_t)(b * a.Hkv + g) * nk * D;
+    const uint16_t* Qp = (const uint16_t*)a.Q + (size_t)bh * nq * D;
+    const uint16_t* Kp = (const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D;
+    const uint16_t* Vp = (const uint16_t*)a.V + (size_t)(b * a.Hkv + g) * nk * D;
+    const __amdgpu_buffer_rsrc_t Krs = make_rsrc(Kp, (uint32_t)nk * D * 2);
+    const __amdgpu_buffer_rsrc_t Vrs = make_rsrc(Vp, (uint32_t)nk * D * 2);
 
-  // Q rows of this wave as B operands: lane holds query qi, features
-  // 16kk + 8h32 .. +7
-  vec8 qreg[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (qi < nq) v = *(const u32x4*)(Qp + (size_t)qi * D + 16 * kk + 8 * h32);
-    qreg[kk] = as_vec8<E>(v);
-  }
-
-  f32x16 oacc[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[md][r] = 0.f;
-  float mref = kNegInf, lsum = 0.f;
-
-  // key-tile range of the workgroup
-  const int qlast = min(q0 + BQ, nq) - 1;
-  int jt_lo = 0, jt_hi = (nk - 1) / BK;
-  if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
-  if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
-
-  const TileCopy<BK, D, NW> tcopy(wave, lane);
-  constexpr int NCOPY = 2 * TileCopy<BK, D, NW>::PER_WAVE;  // copy instructions per wave per tile
-  // copy instruction u of tile jt into stage st: K rows first, then V rows
-  // (rows past nk read row nk-1; those keys are masked as a ragged tile)
-  auto copy_one = [&](int jt, auto st, int u) __attribute__((always_inline)) {
-    constexpr int PW = TileCopy<BK, D, NW>::PER_WAVE;
-    if (u < PW) tcopy.issue_one(kbuf(st), Kp, jt * BK, nk - 1, u);
-    else tcopy.issue_one(vbuf(st), Vp, jt * BK, nk - 1, u - PW);
-  };
-
-  const float sl2 = a.scale_log2;
-  const RowOps32<ROWB> kops(lane);
-  const TrOps32<ROWB> vops(lane);
-
-  // ---------------------------------------------------------------- pieces
-  // MFMA operand t of a tile, in slot order: K rows for S(0) (t < KS) and
-  // S(1) (t < 2KS), then V^T for PV(0) and PV(1), each in (kh, md) order
-  constexpr int NOPS = 2 * KS + 4 * MD;
-  auto operand = [&](const char ETS_LDS* kt, const char ETS_LDS* vt, int t) __attribute__((always_inline)) {
-    if (t < 2 * KS) return as_vec8<E>(lds_b128(kt, kops.off(32 * (t / KS), t % KS)));
-    const int u = t - 2 * KS, mb = u / (2 * MD), kh = (u / MD) % 2, md = u % MD;
-    return as_vec8<E>(vops.read(vt, 32 * mb + 16 * kh, md));
-  };
-
-  // Online summary step for one 32-key block, split into 7 parts that are
-  // spread over MFMA slots.  Block keys of accumulator entry r: key0 + 8(r/4)
-  // + 4h32 + r%4 with key0 = j0 + 32mb.
-  struct Summary {
-    float mx, alpha, mneg;
-    bool need;
-    uint32_t packed[8];
-  };
-  auto summary_part = [&](Summary& st, const f32x16& s, auto part_c, int key0) __attribute__((always_inline)) {
-    constexpr int part = decltype(part_c)::value;
-    if constexpr (part == 0) {
-      st.mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-#pragma unroll
-      for (int r = 4; r < 8; ++r) st.mx = fmaxf(st.mx, s[r]);
-    } else if constexpr (part == 1) {
-#pragma unroll
-      for (int r = 8; r < 16; ++r) st.mx = fmaxf(st.mx, s[r]);
-    } else if constexpr (part == 2) {
-      const float mx = xhalf_max(st.mx);
-      const float mt = mx * sl2;
-      st.need = mt > mref + kRescaleSlack;
-      st.alpha = st.need ? fast_exp2(mref - mt) : 1.f;
-      mref = st.need ? mt : mref;
-      lsum *= st.alpha;
-      st.mneg = -mref;
-    } else {
-      constexpr int g4 = part - 3;  // 0..3: accumulator entries 4g4 .. 4g4+3
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(s[4 * g4 + r], sl2, st.mneg));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lsum += p[r];  // the normaliser counts dropped weights too
-      if constexpr (DROP) {
-        const unsigned keep = keep4(a.drop, bh, qi, key0 + 8 * g4 + 4 * h32);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!((keep >> r) & 1u)) p[r] = 0.f;
-      }
-      st.packed[2 * g4] = E::pack2(p[0], p[1]);
-      st.packed[2 * g4 + 1] = E::pack2(p[2], p[3]);
-      // computed here, not sunk to the PV product behind the rescale branch
-      // or to the end of the loop
-      materialize(st.packed[2 * g4]);
-      materialize(st.packed[2 * g4 + 1]);
-      materialize(lsum);
+    // Q rows of this wave as B operands: lane holds query qi, features
+    // 16kk + 8h32 .. +7
+    vec8 qreg[KS];
+  #pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (qi < nq) v = *(const u32x4*)(Qp + (size_t)qi * D + 16 * kk + 8 * h32);
+      qreg[kk] = as_vec8<E>(v);
     }
-  };
-  // P^T operand for k-step kh (16 keys) of a block: accumulator entries 8kh .. 8kh+7
-  auto pt_operand = [&](const Summary& st, int kh) __attribute__((always_inline)) {
-    return as_vec8<E>(u32x4{st.packed[4 * kh], st.packed[4 * kh + 1], st.packed[4 * kh + 2], st.packed[4 * kh + 3]});
-  };
-  auto rescale = [&](const Summary& st) __attribute__((always_inline)) {
-    if (wave_any(st.need)) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[md][r] *= st.alpha;
-    }
-  };
 
-  // ------------------------------------------ tile every row sees whole
-  // One MFMA per slot, operands read two slots ahead, the copy of the next
-  // tile in the S(0) slots, summary(0) in the S(1) slots and summary(1) in
-  // the PV(0) slots.  Fences keep the compiler from regrouping the slots.
-  constexpr int NSLOT = NOPS;  // one MFMA per operand
-  auto full_tile = [&](auto st, int jt, int jnext) __attribute__((always_inline)) {
-    const char ETS_LDS* kt = kbuf(st);
-    const char ETS_LDS* vt = vbuf(st);
-    typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
-    const int j0 = jt * BK;
-    f32x16 s0, s1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-    Summary sm0, sm1;
-    vec8 opb[3];
-    opb[0] = operand(kt, vt, 0);
-    opb[1] = operand(kt, vt, 1);
-    static_for<NSLOT>([&](auto tc) __attribute__((always_inline)) {
-      constexpr int t = decltype(tc)::value;
-      if constexpr (t + 2 < NOPS) opb[(t + 2) % 3] = operand(kt, vt, t + 2);
-      const vec8 op = opb[t % 3];
-      if constexpr (t < KS) {
-        s0 = E::mfma32(op, qreg[t], s0);
-        static_for<NCOPY>([&](auto uc) __attribute__((always_inline)) {
-          constexpr int u = decltype(uc)::value;
-          if constexpr ((u * KS) / NCOPY == t) copy_one(jnext, Next{}, u);
-        });
-      } else if constexpr (t < 2 * KS) {
-        s1 = E::mfma32(op, qreg[t - KS], s1);
-        static_for<7>([&](auto pc) __attribute__((always_inline)) {
-          if constexpr ((decltype(pc)::value * KS) / 7 == t - KS) summary_part(sm0, s0, pc, j0);
-        });
-        if constexpr (t == 2 * KS - 1) {
-          ETS_FENCE();
-          rescale(sm0);
-        }
-      } else if constexpr (t < 2 * KS + 2 * MD) {
-        constexpr int u = t - 2 * KS;
-        oacc[u % MD] = E::mfma32(op, pt_operand(sm0, u / MD), oacc[u % MD]);
-        static_for<7>([&](auto pc) __attribute__((always_inline)) {
-          if constexpr ((decltype(pc)::value * 2 * MD) / 7 == u) summary_part(sm1, s1, pc, j0 + 32);
-        });
-        if constexpr (t == 2 * KS + 2 * MD - 1) {
-          ETS_FENCE();
-          rescale(sm1);
+    f32x16 oacc[MD];
+  #pragma unroll
+    for (int md = 0; md < MD; ++md)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[md][r] = 0.f;
+    float mref = kNegInf, lsum = 0.f;
+
+    // key-tile range of the workgroup
+    const int qlast = min(q0 + BQ, nq) - 1;
+    int jt_lo = 0, jt_hi = (nk - 1) / BK;
+    if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
+    if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
+
+    const TileCopy<BK, D, NW> tcopy(wave, lane);
+    constexpr int NCOPY = 2 * TileCopy<BK, D, NW>::PER_WAVE;  // copy instructions per wave per tile
+    // copy instruction u of tile jt into stage st: K rows first, then V rows
+    // (rows past nk read row nk-1; those keys are masked as a ragged tile)
+    auto copy_one = [&](int jt, auto st, int u) __attribute__((always_inline)) {
+      constexpr int PW = TileCopy<BK, D, NW>::PER_WAVE;
+      if (u < PW) tcopy.issue_one(kbuf(st), Krs, jt * BK, nk - 1, u);
+      else tcopy.issue_one(vbuf(st), Vrs, jt * BK, nk - 1, u - PW);
+    };
+
+    const float sl2 = a.scale_log2;
+    const RowOps32<ROWB> kops(lane);
+    const TrOps32<ROWB> vops(lane);
+
+    // ---------------------------------------------------------------- pieces
+    // MFMA operand t of a tile, in slot order: K rows for S(0) (t < KS) and
+    // S(1) (t < 2KS), then V^T for PV(0) and PV(1), each in (kh, md) order
+    constexpr int NOPS = 2 * KS + 4 * MD;
+    auto operand = [&](const char ETS_LDS* kt, const char ETS_LDS* vt, int t) __attribute__((always_inline)) {
+      if (t < 2 * KS) return as_vec8<E>(lds_b128(kt, kops.off(32 * (t / KS), t % KS)));
+      const int u = t - 2 * KS, mb = u / (2 * MD), kh = (u / MD) % 2, md = u % MD;
+      return as_vec8<E>(vops.read(vt, 32 * mb + 16 * kh, md));
+    };
+
+    // Online summary step for one 32-key block, split into 7 parts that are
+    // spread over MFMA slots.  Block keys of accumulator entry r: key0 + 8(r/4)
+    // + 4h32 + r%4 with key0 = j0 + 32mb.  In a masked block (PART) the scores
+    // are scaled to base 2 first and disallowed ones set to -inf, so a row with
+    // no allowed key in the block raises nothing and gets zero weights.
+    struct Summary {
+      float mx, alpha, mneg;
+      bool need;
+      uint32_t packed[8];
+    };
+    // allowed keys of this lane's row form one interval for arithmetic masks:
+    // key0 + c allowed iff lo <= c <= lo + rng (unsigned compare of c - lo)
+    auto arith_interval = [&](int key0, int& lo, unsigned& rng) __attribute__((always_inline)) {
+      int jlo = 0, jhi = nk - 1;
+      if (a.mask.causal) jhi = min(jhi, qi);
+      if (a.mask.window > 0) jlo = max(jlo, qi - a.mask.window + 1);
+      const int base = key0 + 4 * h32;
+      const bool any = qi < nq && jlo <= jhi;
+      lo = any ? jlo - base : (1 << 24);
+      rng = any ? (unsigned)(jhi - jlo) : 0u;
+    };
+    auto mask_scale = [&](f32x16& s, int r0, int key0, bool cbm) __attribute__((always_inline)) {
+      if constexpr (MK == kArith) {
+        int lo;
+        unsigned rng;
+        arith_interval(key0, lo, rng);
+  #pragma unroll
+        for (int r = r0; r < r0 + 8; ++r) {
+          const int c = 8 * (r / 4) + r % 4;
+          s[r] = ((unsigned)(c - lo) <= rng) ? s[r] * sl2 : kNegInf;
         }
       } else {
-        constexpr int u = t - 2 * KS - 2 * MD;
-        oacc[u % MD] = E::mfma32(op, pt_operand(sm1, u / MD), oacc[u % MD]);
-      }
-      ETS_FENCE();
-    });
-  };
-
-  // --------------------------------------------- general (masked) tile
-  // The same steps with the mask applied; kPartial or kFull per wave, with
-  // the compiler's own interleaving.
-  auto masked_tile = [&](auto st, int jt, int jnext, int cls, bool cbm) __attribute__((always_inline)) {
-    const char ETS_LDS* kt = kbuf(st);
-    const char ETS_LDS* vt = vbuf(st);
-    typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
-    const int j0 = jt * BK;
-#pragma unroll
-    for (int u = 0; u < NCOPY; ++u) copy_one(jnext, Next{}, u);
-    if (cls == kEmpty) return;
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) s[mb] = E::mfma32(operand(kt, vt, KS * mb + kk), qreg[kk], s[mb]);
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int key0 = j0 + 32 * mb;
-      if (cls == kPartial) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
+  #pragma unroll
+        for (int g4 = r0 / 4; g4 < r0 / 4 + 2; ++g4) {
           const unsigned allow = allowed4<MK>(a.mask, qi, key0 + 8 * g4 + 4 * h32, nq, nk, cbm);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!((allow >> r) & 1u)) s[mb][4 * g4 + r] = kNegInf;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) s[4 * g4 + r] = ((allow >> r) & 1u) ? s[4 * g4 + r] * sl2 : kNegInf;
         }
       }
-      // a row with no allowed key in this block keeps its summary: its
-      // maximum is -inf, it raises nothing and all its weights are zero
-      Summary sm;
-      summary_part(sm, s[mb], std::integral_constant<int, 0>{}, key0);
-      summary_part(sm, s[mb], std::integral_constant<int, 1>{}, key0);
-      {
-        const float mx = xhalf_max(sm.mx);
-        const float mt = (mx == kNegInf) ? kNegInf : mx * sl2;
-        sm.need = mt > mref + kRescaleSlack;
-        sm.alpha = sm.need ? fast_exp2(mref - mt) : 1.f;
-        mref = sm.need ? mt : mref;
-        lsum *= sm.alpha;
-        sm.mneg = -mref;
-      }
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
+    };
+    auto summary_part = [&](Summary& st, f32x16& s, auto part_c, auto part_tag, int key0, bool cbm)
+                            __attribute__((always_inline)) {
+      constexpr int part = decltype(part_c)::value;
+      constexpr bool PART = decltype(part_tag)::value;
+      if constexpr (part == 0) {
+        if constexpr (PART) mask_scale(s, 0, key0, cbm);
+        st.mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  #pragma unroll
+        for (int r = 4; r < 8; ++r) st.mx = fmaxf(st.mx, s[r]);
+      } else if constexpr (part == 1) {
+        if constexpr (PART) mask_scale(s, 8, key0, cbm);
+  #pragma unroll
+        for (int r = 8; r < 16; ++r) st.mx = fmaxf(st.mx, s[r]);
+      } else if constexpr (part == 2) {
+        const float mx = xhalf_max(st.mx);
+        const float mt = PART ? mx : mx * sl2;
+        st.need = mt > mref + kRescaleSlack;
+        st.alpha = st.need ? fast_exp2(mref - mt) : 1.f;
+        mref = st.need ? mt : mref;
+        lsum *= st.alpha;
+        st.mneg = (PART && mref == kNegInf) ? 0.f : -mref;
+      } else {
+        constexpr int g4 = part - 3;  // 0..3: accumulator entries 4g4 .. 4g4+3
         float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = fast_exp2(fmaf(s[mb][4 * g4 + r], sl2, sm.mneg));
-          if (s[mb][4 * g4 + r] == kNegInf) p[r] = 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lsum += p[r];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r)
+          p[r] = PART ? fast_exp2(s[4 * g4 + r] + st.mneg) : fast_exp2(fmaf(s[4 * g4 + r], sl2, st.mneg));
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) lsum += p[r];  // the normaliser counts dropped weights too
         if constexpr (DROP) {
           const unsigned keep = keep4(a.drop, bh, qi, key0 + 8 * g4 + 4 * h32);
-#pragma unroll
+  #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (!((keep >> r) & 1u)) p[r] = 0.f;
         }
-        sm.packed[2 * g4] = E::pack2(p[0], p[1]);
-        sm.packed[2 * g4 + 1] = E::pack2(p[2], p[3]);
+        st.packed[2 * g4] = E::pack2(p[0], p[1]);
+        st.packed[2 * g4 + 1] = E::pack2(p[2], p[3]);
+        // computed here, not sunk to the PV product behind the rescale branch
+        // or to the end of the loop
+        materialize(st.packed[2 * g4]);
+        materialize(st.packed[2 * g4 + 1]);
+        materialize(lsum);
       }
-      rescale(sm);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
+    };
+    // P^T operand for k-step kh (16 keys) of a block: accumulator entries 8kh .. 8kh+7
+    auto pt_operand = [&](const Summary& st, int kh) __attribute__((always_inline)) {
+      return as_vec8<E>(u32x4{st.packed[4 * kh], st.packed[4 * kh + 1], st.packed[4 * kh + 2], st.packed[4 * kh + 3]});
+    };
+    auto rescale = [&](const Summary& st) __attribute__((always_inline)) {
+      if (wave_any(st.need)) {
+  #pragma unroll
         for (int md = 0; md < MD; ++md)
-          oacc[md] = E::mfma32(operand(kt, vt, 2 * KS + 2 * MD * mb + MD * kh + md), pt_operand(sm, kh), oacc[md]);
-    }
-  };
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[md][r] *= st.alpha;
+      }
+    };
 
-  // ------------------------------------------------------------- the loop
-  // The workgroup's non-empty tiles in key order, tile number p on ring stage
-  // p % 2; the copy of the next tile is issued during the current one (in the
-  // last one the current tile is copied again into the idle stage, which
-  // keeps the issue free of branches).  For arithmetic masks the tiles are
-  // jt_lo .. jt_hi, and those every row of the workgroup sees whole form one
-  // range; pairs of them starting on stage 0 take the fixed-order path.
-  auto wg_nonempty = [&](int jt) {
-    return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
-  };
-  auto next_of = [&](int jt) {
+    // ------------------------------------------------------------- one tile
+    // One MFMA per slot, operands read two slots ahead, the copy of the next
+    // tile in the S(0) slots, summary(0) in the S(1) slots and summary(1) in
+    // the PV(0) slots.  Fences keep the compiler from regrouping the slots.
+    // part_tag: masked tile (the wave's rows see only part of it) or whole.
+    constexpr int NSLOT = NOPS;  // one MFMA per operand
+    auto tile = [&](auto st, int jt, int jnext, auto part_tag, bool cbm) __attribute__((always_inline)) {
+      const char ETS_LDS* kt = kbuf(st);
+      const char ETS_LDS* vt = vbuf(st);
+      typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
+      const int j0 = jt * BK;
+      f32x16 s0, s1;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+      Summary sm0, sm1;
+      vec8 opb[3];
+      opb[0] = operand(kt, vt, 0);
+      opb[1] = operand(kt, vt, 1);
+      static_for<NSLOT>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (t + 2 < NOPS) opb[(t + 2) % 3] = operand(kt, vt, t + 2);
+        const vec8 op = opb[t % 3];
+        if constexpr (t < KS) {
+          s0 = E::mfma32(op, qreg[t], s0);
+          static_for<NCOPY>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            if constexpr ((u * KS) / NCOPY == t) copy_one(jnext, Next{}, u);
+          });
+        } else if constexpr (t < 2 * KS) {
+          s1 = E::mfma32(op, qreg[t - KS], s1);
+          static_for<7>([&](auto pc) __attribute__((always_inline)) {
+            if constexpr ((decltype(pc)::value * KS) / 7 == t - KS) summary_part(sm0, s0, pc, part_tag, j0, cbm);
+          });
+          if constexpr (t == 2 * KS - 1) {
+            ETS_FENCE();
+            rescale(sm0);
+          }
+        } else if constexpr (t < 2 * KS + 2 * MD) {
+          constexpr int u = t - 2 * KS;
+          oacc[u % MD] = E::mfma32(op, pt_operand(sm0, u / MD), oacc[u % MD]);
+          static_for<7>([&](auto pc) __attribute__((always_inline)) {
+            if constexpr ((decltype(pc)::value * 2 * MD) / 7 == u) summary_part(sm1, s1, pc, part_tag, j0 + 32, cbm);
+          });
+          if constexpr (t == 2 * KS + 2 * MD - 1) {
+            ETS_FENCE();
+            rescale(sm1);
+          }
+        } else {
+          constexpr int u = t - 2 * KS - 2 * MD;
+          oacc[u % MD] = E::mfma32(op, pt_operand(sm1, u / MD), oacc[u % MD]);
+        }
+        ETS_FENCE();
+      });
+    };
+
+    // a tile none of the wave's rows sees: only the copy of the next tile
+    auto empty_tile = [&](auto st, int jnext) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
+  #pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(jnext, Next{}, u);
+    };
+
+    // ------------------------------------------------------------- the loop
+    // The workgroup's non-empty tiles in key order, tile number p on ring stage
+    // p % 2; the copy of the next tile is issued during the current one (in the
+    // last one the current tile is copied again into the idle stage, which
+    // keeps the issue free of branches).  For arithmetic masks the tiles are
+    // jt_lo .. jt_hi, and those every row of the workgroup sees whole form one
+    // range; pairs of them starting on stage 0 take the fixed-order path.
+    auto wg_nonempty = [&](int jt) {
+      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
+    };
+    auto next_of = [&](int jt) {
+      if constexpr (MK == kArith) {
+        return jt < jt_hi ? jt + 1 : -1;
+      } else {
+        for (++jt; jt <= jt_hi; ++jt)
+          if (wg_nonempty(jt)) return jt;
+        return -1;
+      }
+    };
+    int jt = -1;
+    if (jt_lo <= jt_hi) jt = (MK == kArith || wg_nonempty(jt_lo)) ? jt_lo : next_of(jt_lo);
+
+    int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
     if constexpr (MK == kArith) {
-      return jt < jt_hi ? jt + 1 : -1;
-    } else {
-      for (++jt; jt <= jt_hi; ++jt)
-        if (wg_nonempty(jt)) return jt;
-      return -1;
-    }
-  };
-  int jt = -1;
-  if (jt_lo <= jt_hi) jt = (MK == kArith || wg_nonempty(jt_lo)) ? jt_lo : next_of(jt_lo);
-
-  int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
-  if constexpr (MK == kArith) {
-    if (q0 + BQ <= nq) {
-      int f_lo = jt_lo, f_hi = min(jt_hi, nk / BK - 1);
-      if (a.mask.causal) f_hi = min(f_hi, q0 >= BK - 1 ? (q0 - (BK - 1)) / BK : -1);
-      if (a.mask.window > 0) {
-        const int t = q0 + BQ - 1 - a.mask.window;  // full iff j0 > t
-        if (t >= 0) f_lo = max(f_lo, t / BK + 1);
-      }
-      if (f_lo <= f_hi) {
-        const int lo = f_lo - jt_lo, hi = f_hi - jt_lo + 1;
-        const int p0 = lo + (lo & 1), p1 = hi - ((hi - p0) & 1);
-        if (p0 < p1) { fp0 = p0; fp1 = p1; }
+      if (q0 + BQ <= nq) {
+        int f_lo = jt_lo, f_hi = min(jt_hi, nk / BK - 1);
+        if (a.mask.causal) f_hi = min(f_hi, q0 >= BK - 1 ? (q0 - (BK - 1)) / BK : -1);
+        if (a.mask.window > 0) {
+          const int t = q0 + BQ - 1 - a.mask.window;  // full iff j0 > t
+          if (t >= 0) f_lo = max(f_lo, t / BK + 1);
+        }
+        if (f_lo <= f_hi) {
+          const int lo = f_lo - jt_lo, hi = f_hi - jt_lo + 1;
+          const int p0 = lo + (lo & 1), p1 = hi - ((hi - p0) & 1);
+          if (p0 < p1) { fp0 = p0; fp1 = p1; }
+        }
       }
     }
-  }
 
-  // prologue: the first tile into stage 0
-  if (jt >= 0) {
-#pragma unroll
-    for (int u = 0; u < NCOPY; ++u) copy_one(jt, Stage0{}, u);
-  }
-  wait_vm();
-  __syncthreads();
-
-  auto finish = [&]() __attribute__((always_inline)) {
-    wait_vm();  // this wave's part of the next tile has landed
+    // prologue: the first tile into stage 0
+    if (jt >= 0) {
+  #pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(jt, Stage0{}, u);
+    }
+    wait_vm();
     __syncthreads();
-  };
-  auto general_step = [&](auto st, int jt, int jn) __attribute__((always_inline)) {
-    const int j0 = jt * BK;
-    const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nq, nk);
-    const int cls = cinfo & kClassMask;
-    if (cls == kFull) full_tile(st, jt, jn);
-    else masked_tile(st, jt, jn, cls, (cinfo & kCheckBlockMask) != 0);
-    finish();
-  };
-  int p = 0;
-  auto general_run = [&](int p_end) __attribute__((always_inline)) {
-    for (; jt >= 0 && p < p_end; ++p) {
-      const int jn = next_of(jt);
-      if (p & 1) general_step(Stage1{}, jt, jn >= 0 ? jn : jt);
-      else general_step(Stage0{}, jt, jn >= 0 ? jn : jt);
-      jt = jn;
-    }
-  };
-  general_run(fp0);
-  if (fp0 < fp1) {
-    // a fixed-order range exists (arithmetic masks only): general_run stopped
-    // at tile number fp0 < N, so jt = jt_lo + p here and tile p + 1 is full too
-    for (; p < fp1; p += 2) {
-      full_tile(Stage0{}, jt, jt + 1);
-      finish();
-      const int jn = next_of(jt + 1);
-      full_tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1);
-      finish();
-      jt = jn;
-    }
-  }
-  general_run(1 << 30);
 
-  // ---- epilogue: Y = z / l, LSE = (m + log2 l) ln 2
-  uint16_t* Yp = (uint16_t*)a.out_Y + (size_t)bh * nq * D;
-  float* Lp = a.LSE + (size_t)bh * nq;
-  const float l = xhalf_sum(lsum);
-  float inv = (l > 0.f) ? 1.f / l : 0.f;
-  if constexpr (DROP) inv *= a.drop.inv_keep;
-  if (qi < nq) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int col = 32 * md + 8 * g4 + 4 * h32;
-        u32x2 w;
-        w[0] = E::pack2(oacc[md][4 * g4] * inv, oacc[md][4 * g4 + 1] * inv);
-        w[1] = E::pack2(oacc[md][4 * g4 + 2] * inv, oacc[md][4 * g4 + 3] * inv);
-        *(u32x2*)(Yp + (size_t)qi * D + col) = w;
+    auto finish = [&]() __attribute__((always_inline)) {
+      wait_vm();  // this wave's part of the next tile has landed
+      __syncthreads();
+    };
+    auto general_step = [&](auto st, int jt, int jn) __attribute__((always_inline)) {
+      const int j0 = jt * BK;
+      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nq, nk);
+      const int cls = cinfo & kClassMask;
+      if (cls == kFull) tile(st, jt, jn, std::false_type{}, false);
+      else if (cls == kPartial) tile(st, jt, jn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      else empty_tile(st, jn);
+      finish();
+    };
+    int p = 0;
+    auto general_run = [&](int p_end) __attribute__((always_inline)) {
+      for (; jt >= 0 && p < p_end; ++p) {
+        const int jn = next_of(jt);
+        if (p & 1) general_step(Stage1{}, jt, jn >= 0 ? jn : jt);
+        else general_step(Stage0{}, jt, jn >= 0 ? jn : jt);
+        jt = jn;
       }
-    if (h32 == 0) Lp[qi] = (l > 0.f) ? (mref + __log2f(l)) * kLn2 : kNegInf;
+    };
+    general_run(fp0);
+    if (fp0 < fp1) {
+      // a fixed-order range exists (arithmetic masks only): general_run stopped
+      // at tile number fp0 < N, so jt = jt_lo + p here and tile p + 1 is full too
+      for (; p < fp1; p += 2) {
+        tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
+        finish();
+        const int jn = next_of(jt + 1);
+        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, std::false_type{}, false);
+        finish();
+        jt = jn;
+      }
+    }
+    general_run(1 << 30);
+
+    // ---- epilogue: Y = z / l, LSE = (m + log2 l) ln 2
+    uint16_t* Yp = (uint16_t*)a.out_Y + (size_t)bh * nq * D;
+    float* Lp = a.LSE + (size_t)bh * nq;
+    const float l = xhalf_sum(lsum);
+    float inv = (l > 0.f) ? 1.f / l : 0.f;
+    if constexpr (DROP) inv *= a.drop.inv_keep;
+    if (qi < nq) {
+  #pragma unroll
+      for (int md = 0; md < MD; ++md)
+  #pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * md + 8 * g4 + 4 * h32;
+          u32x2 w;
+          w[0] = E::pack2(oacc[md][4 * g4] * inv, oacc[md][4 * g4 + 1] * inv);
+          w[1] = E::pack2(oacc[md][4 * g4 + 2] * inv, oacc[md][4 * g4 + 3] * inv);
+          *(u32x2*)(Yp + (size_t)qi * D + col) = w;
+        }
+      if (h32 == 0) Lp[qi] = (l > 0.f) ? (mref + __log2f(l)) * kLn2 : kNegInf;
+    }
   }
+}
+
+template <class E, int D, int NW, int MK, bool DROP>
+static int launch_fwd_k(const DenseArgs& a, void* stream) {
+  constexpr int BQ = NW * 32;
+  const int n_qtiles = (a.nq + BQ - 1) / BQ;
+  const int n_items = n_qtiles * a.B * a.H;
+  int slots = 0;
+  ETS_TRY(resident_slots(dense_fwd_kernel<E, D, NW, MK, DROP>, 64 * NW, &slots));
+  dim3 grid(min(n_items, slots)), block(64 * NW);
+  ETS_TRY(launch((dense_fwd_kernel<E, D, NW, MK, DROP>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
+  return 0;
 }
 
 template <class E, int D, int NW, int MK>
 static int launch_fwd_mk(const DenseArgs& a, void* stream) {
-  constexpr int BQ = NW * 32;
-  const int n_qtiles = (a.nq + BQ - 1) / BQ;
-  dim3 grid(n_qtiles * a.B * a.H), block(64 * NW);
-  if (a.drop.enabled)
-    ETS_TRY(launch((dense_fwd_kernel<E, D, NW, MK, true>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
-  else
-    ETS_TRY(launch((dense_fwd_kernel<E, D, NW, MK, false>), grid, block, 0, (hipStream_t)stream, a, n_qtiles));
-  return 0;
+  if (a.drop.enabled) return launch_fwd_k<E, D, NW, MK, true>(a, stream);
+  return launch_fwd_k<E, D, NW, MK, false>(a, stream);
 }
 
 template <class E, int D, int NW>

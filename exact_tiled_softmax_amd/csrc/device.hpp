@@ -40,6 +40,29 @@ inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds
   return hipLaunchKernel((const void*)kernel, grid, block, ptrs, lds, st);
 }
 
+// Workgroups of `kernel` that the device keeps resident at once (compute
+// units x workgroups per unit), cached per device.  Persistent kernels launch
+// at most this many workgroups.
+template <class... P>
+inline hipError_t resident_slots(void (*kernel)(P...), int block_threads, int* slots) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *slots = cache[dev];
+    return hipSuccess;
+  }
+  int per_cu = 0, cus = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, block_threads, 0);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  *slots = per_cu > 0 && cus > 0 ? per_cu * cus : 1;
+  if (dev >= 0 && dev < 64) cache[dev] = *slots;
+  return hipSuccess;
+}
+
 #define ETS_TRY(expr)                      \
   do {                                     \
     const hipError_t ets_e_ = (expr);      \
@@ -158,16 +181,31 @@ __device__ __forceinline__ u32x4 lds_tr8(const char ETS_LDS* base, int r0, int r
   return __builtin_bit_cast(u32x4, v);
 }
 
+// Buffer resource for the raw buffer instructions: `bytes` bytes from `base`
+// (reads past them return zero).  Dword 3 selects 32-bit data format, as the
+// raw (untyped) loads require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane l writes
+// at ldsdst + 16 l.  The MUBUF form (buffer_load_dwordx4 ... lds) is used
+// rather than global_load_lds: with a FLAT-encoded copy in flight the compiler
+// makes every later LDS read wait for all outstanding LDS traffic
+// (lgkmcnt(0)), while with the buffer form it keeps exact counts.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, void ETS_LDS* ldsdst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ldsdst, 16, byte_off, 0, 0, 0);
+}
+
 // Direct global -> LDS copy of a tile of ROWS rows x W 16-bit elements into
-// the swizzled tile format (global_load_lds_dwordx4: lane l of a wave writes
-// 16 bytes at the instruction's LDS base + 16 l).  Each of the NWAVES waves
-// issues ROWS*W/8/64/NWAVES instructions; lane l of instruction k fills chunk
+// the swizzled tile format.  Each of the NWAVES waves issues
+// ROWS*W/8/64/NWAVES instructions; lane l of instruction k fills chunk
 // position 64k + l, so it fetches the logical chunk that the swizzle maps
 // there.  Rows past last_row are read from last_row instead (finite data; the
 // caller masks them), so no access leaves the tensor.  Completion is awaited
 // with a vmcnt wait before the barrier that publishes the tile.  The per-lane
-// parts of the addresses are computed once; an issue costs three VALU
-// operations per instruction (row clamp and byte offset from a scalar base).
+// parts of the offsets are computed once; an issue costs three VALU
+// operations per instruction (row clamp and byte offset).
 template <int ROWS, int W, int NWAVES>
 struct TileCopy {
   static constexpr int CPR = W / 8;  // 16-byte chunks per row
@@ -184,23 +222,18 @@ struct TileCopy {
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) col[u] = phys_chunk<2 * W>(row + u * RPI, lane % CPR) * 16;  // involution
   }
-  // instruction u (0 .. PER_WAVE-1) of the wave's share
-  __device__ __forceinline__ void issue_one(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row,
+  // instruction u (0 .. PER_WAVE-1) of the wave's share; rs covers the tensor
+  // whose row 0 is at offset 0
+  __device__ __forceinline__ void issue_one(char ETS_LDS* dst, __amdgpu_buffer_rsrc_t rs, int row0, int last_row,
                                             int u) const {
     const unsigned off = (unsigned)min(row0 + row + u * RPI, last_row) * (unsigned)(2 * W) + (unsigned)col[u];
-    __builtin_amdgcn_global_load_lds((const char*)base + off, (void ETS_LDS*)(dst + (inst0 + u) * 1024), 16, 0, 0);
+    copy16_to_lds(rs, off, (void ETS_LDS*)(dst + (inst0 + u) * 1024));
   }
-  __device__ __forceinline__ void issue(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row) const {
+  __device__ __forceinline__ void issue(char ETS_LDS* dst, __amdgpu_buffer_rsrc_t rs, int row0, int last_row) const {
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) issue_one(dst, base, row0, last_row, u);
+    for (int u = 0; u < PER_WAVE; ++u) issue_one(dst, rs, row0, last_row, u);
   }
 };
-
-template <int ROWS, int W, int NWAVES>
-__device__ __forceinline__ void tile_to_lds(char ETS_LDS* dst, const uint16_t* base, int row0, int last_row,
-                                            int wave, int lane) {
-  TileCopy<ROWS, W, NWAVES>(wave, lane).issue(dst, base, row0, last_row);
-}
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
