@@ -6,6 +6,13 @@ the three backward launches (prepass, dK/dV, dQ) on the same stream.  Inputs
 are seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-probe     # plain device copy of known size, for scaling HBM counters
+
+The roofline object's "traffic" (HBM bytes per launch of the dominant kernel)
+comes from profiles/<kernel>_<workload>_traffic.md, written from rocprofv3
+FETCH_SIZE / WRITE_SIZE runs scaled by what the same counters read for the
+copy probe; it is reported only while the kernel's sources still hash to the
+value recorded there, else null.
 
 Flops are algorithmic: only allowed (query, key) pairs count.  Per pair the
 forward does 2d + 2dv flops (S = c Q K^T, then P V) and the backward 6d + 4dv
@@ -28,6 +35,12 @@ sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
 
+KERNEL_SOURCES = {
+    "fwd": ["exact_tiled_softmax_amd/csrc/dense_fwd.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+    "bwd_dkdv": ["exact_tiled_softmax_amd/csrc/dense_bwd.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+    "bwd_dq": ["exact_tiled_softmax_amd/csrc/dense_bwd.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+    "sparse_fwd": ["exact_tiled_softmax_amd/csrc/sparse.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+}
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA peaks (fp32: vector)
 PEAK_HBM_GBS = 8000.0
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
@@ -36,6 +49,49 @@ METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak (causal, seq 2048, d=12
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha256(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch (fetch + write) recorded for this kernel and
+    workload, or None when absent or taken from different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    try:
+        if vals["source_sha256"] != sources_sha256(kernel):
+            return None
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """Copies 256 MiB device to device five times (torch's copy kernel): the
+    known traffic per dispatch (256 MiB read, 256 MiB written) scales the
+    FETCH_SIZE / WRITE_SIZE counters of the attention kernels."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "dispatches": 5}), flush=True)
 
 
 def dense_pairs(w, block_mask):
@@ -154,7 +210,7 @@ def bench_dense(w, args):
             kernels[n] = {"ms": kern_ms[n], "TFLOP/s": tf, "frac_peak": tf / peak}
     dom = max(["fwd", "bwd_dkdv", "bwd_dq"], key=lambda n: kern_ms[n])
     roofline = {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": peak, "unit": "TFLOP/s",
-                "frac": kernels[dom]["TFLOP/s"] / peak, "traffic": None, "kernel": dom,
+                "frac": kernels[dom]["TFLOP/s"] / peak, "traffic": recorded_traffic(dom, w.name), "kernel": dom,
                 "flops_per_launch": flops[dom]}
     fwd_tf = f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
     bwd_ms = kern_ms["bwd_prep"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
@@ -260,7 +316,8 @@ def bench_sparse(w, args):
         "bwd": {"ms": b_ms, "TFLOP/s": fl_b / (b_ms * 1e-3) / 1e12,
                 "gathered_GB/s": 2 * gathered / (b_ms * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": fwd_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": fwd_gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "sparse_fwd",
+                     "frac": fwd_gbs / PEAK_HBM_GBS, "traffic": recorded_traffic("sparse_fwd", w.name),
+                     "kernel": "sparse_fwd",
                      "bytes_per_launch": gathered},
     }
     if not args.no_cpu_baseline:
@@ -275,6 +332,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_causal_bf16_b4h16_n2048_d128", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="run only the reference copy (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -285,6 +343,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a visible GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
     w = workloads.WORKLOADS[args.workload]
     if isinstance(w, workloads.DenseWorkload):
         out = bench_dense(w, args)
