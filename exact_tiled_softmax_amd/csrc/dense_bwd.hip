@@ -21,7 +21,8 @@
 //         dV^T += G^T P and dK^T += Q^T gamma directly, with G^T and Q^T read
 //         by LDS transpose reads.  No atomics.
 //   dq    query-major: the forward layout (queries along lanes); recomputes
-//         S^T and dP^T and accumulates dQ^T += K^T gamma^T.  No atomics.
+//         S^T and dP^T and accumulates dQ^T += K^T gamma^T, with K^T read by
+//         LDS transpose reads.  No atomics.
 #include "device.hpp"
 
 namespace ets {
@@ -463,182 +464,260 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
 }
 
 // --------------------------------------------------------------------- dQ
+// Query-major, the forward's layout: a workgroup owns 128 query rows (32 per
+// wave, queries along lanes) of one (batch, head) and streams the K/V tiles
+// of 64 keys through a two-stage LDS ring.  Per 32-key block mb a wave runs
+//   A(mb): S^T = K Q^T and dP^T = V G^T     (2 D/16 MFMAs)
+//   W(mb): gamma^T from S^T, dP^T, LSE, D    (VALU)
+//   B(mb): dQ^T += K^T gamma^T              (2 D/32 MFMAs)
+// in the fixed order A0 | A1+W0 | B0+W1 | B1, one MFMA per slot with
+// operands read two slots ahead; the next tile's copy is spread over A0.
 template <class E, int D, int MK, bool DROP>
-__global__ __launch_bounds__(256, 1) void dense_bwd_dq_kernel(const DenseArgs a, int n_qtiles) {
+__global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a, int n_qtiles) {
   constexpr int BK = 64;
-  constexpr int NQW = 32;
-  constexpr int BQ = 4 * NQW;
+  constexpr int BQ = 128;
   constexpr int KS = D / 16;
   constexpr int MD = D / 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BK * ROWB;
+  constexpr int NA = 2 * KS, NB = 2 * MD;  // slots of A(mb), B(mb)
+  constexpr int NSLOT = 2 * NA + 2 * NB;
   typedef typename E::vec8 vec8;
+  typedef std::integral_constant<int, 0> Stage0;
+  typedef std::integral_constant<int, 1> Stage1;
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * TILEB];
-  char ETS_LDS* smem = (char ETS_LDS*)smem_raw;
+  __shared__ __attribute__((aligned(16))) char ldsK0[TILEB], ldsV0[TILEB], ldsK1[TILEB], ldsV1[TILEB];
+  auto kbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsK0;
+    else return (char ETS_LDS*)ldsK1;
+  };
+  auto vbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsV0;
+    else return (char ETS_LDS*)ldsV1;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int h32 = lane >> 5, l32 = lane & 31;
-  const int BH = a.B * a.H;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
-  const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
   const int nq = a.nq, nk = a.nk;
-  const int q0 = qt * BQ, qw0 = q0 + wave * NQW;
-  const int q = qw0 + l32;
-
-  const uint16_t* Qp = (const uint16_t*)a.Q + (size_t)bh * nq * D;
-  const uint16_t* Gp = (const uint16_t*)a.G + (size_t)bh * nq * D;
-  const uint16_t* Kp = (const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D;
-  const uint16_t* Vp = (const uint16_t*)a.V + (size_t)(b * a.Hkv + g) * nk * D;
-
-  vec8 qreg[KS], greg[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    u32x4 qv = u32x4{0, 0, 0, 0}, gv = u32x4{0, 0, 0, 0};
-    if (q < nq) {
-      qv = *(const u32x4*)(Qp + (size_t)q * D + 16 * kk + 8 * h32);
-      gv = *(const u32x4*)(Gp + (size_t)q * D + 16 * kk + 8 * h32);
-    }
-    qreg[kk] = as_vec8<E>(qv);
-    greg[kk] = as_vec8<E>(gv);
-  }
-  const float lse2 = (q < nq) ? a.Lws[(size_t)bh * nq + q] : __builtin_huge_valf();
-  const float dval = (q < nq) ? a.Dws[(size_t)bh * nq + q] : 0.f;
-
-  f32x16 dq[MD];
-#pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq[md][r] = 0.f;
-
-  const int qlast = min(q0 + BQ, nq) - 1;
-  int jt_lo = 0, jt_hi = (nk - 1) / BK;
-  if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
-  if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
-  auto wg_nonempty = [&](int jt) {
-    return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
-  };
-  auto next_tile = [&](int jt) {
-    for (++jt; jt <= jt_hi; ++jt)
-      if (wg_nonempty(jt)) return jt;
-    return -1;
-  };
-
-  const TileCopy<BK, D, 4> tcopy(wave, lane);
-  const __amdgpu_buffer_rsrc_t Krs = make_rsrc(Kp, (uint32_t)nk * D * 2);
-  const __amdgpu_buffer_rsrc_t Vrs = make_rsrc(Vp, (uint32_t)nk * D * 2);
-  auto load = [&](int jt, int stage) {
-    char ETS_LDS* kt = smem + stage * 2 * TILEB;
-    tcopy.issue(kt, Krs, jt * BK, nk - 1);
-    tcopy.issue(kt + TILEB, Vrs, jt * BK, nk - 1);
-  };
-
-  int jt = (jt_lo <= jt_hi && wg_nonempty(jt_lo)) ? jt_lo : next_tile(jt_lo);
-  int stage = 0;
-  if (jt >= 0) load(jt, 0);
-  wait_vm();
-  __syncthreads();
+  const int BH = a.B * a.H;
   const float sl2 = a.scale_log2;
   const RowOps32<ROWB> rops(lane);
   const TrOps32<ROWB> tops(lane);
+  const TileCopy<BK, D, 4> tcopy(wave, lane);
+  constexpr int PW = TileCopy<BK, D, 4>::PER_WAVE;
+  constexpr int NCOPY = 2 * PW;
 
-  while (jt >= 0) {
-    const int nxt = next_tile(jt);
-    if (nxt >= 0) load(nxt, stage ^ 1);
-    const char ETS_LDS* kt = smem + stage * 2 * TILEB;
-    const char ETS_LDS* vt = kt + TILEB;
-    const int j0 = jt * BK;
-    const int cinfo = classify<MK>(a.mask, qw0, qw0 + NQW - 1, j0, j0 + BK - 1, nq, nk);
-    const int cls = cinfo & kClassMask;
-    const bool cbm = (cinfo & kCheckBlockMask) != 0;
+  // Persistent workgroups over (query tile, (batch, head)), heaviest query
+  // tiles first, in boustrophedon order.
+  const int G = (int)gridDim.x, n_items = n_qtiles * BH;
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (item >= n_items) continue;
+    const int qt = n_qtiles - 1 - item / BH;
+    const int bh = item % BH;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
+    const int q0 = qt * BQ, qw0 = q0 + wave * 32;
+    const int qi = qw0 + l32;  // this lane's query row
 
-    if (cls != kEmpty) {
-      f32x16 sc[2], dp[2];
+    const uint16_t* Qp = (const uint16_t*)a.Q + (size_t)bh * nq * D;
+    const uint16_t* Gp = (const uint16_t*)a.G + (size_t)bh * nq * D;
+    const uint16_t* Kp = (const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D;
+    const uint16_t* Vp = (const uint16_t*)a.V + (size_t)(b * a.Hkv + g) * nk * D;
+    const __amdgpu_buffer_rsrc_t Krs = make_rsrc(Kp, (uint32_t)nk * D * 2);
+    const __amdgpu_buffer_rsrc_t Vrs = make_rsrc(Vp, (uint32_t)nk * D * 2);
+
+    vec8 qreg[KS], greg[KS];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { sc[mb][r] = 0.f; dp[mb][r] = 0.f; }
-      // K and V operands read one k-step ahead of their MFMAs
-      vec8 ka[2][2], va[2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        ka[0][mb] = as_vec8<E>(lds_b128(kt, rops.off(32 * mb, 0)));
-        va[0][mb] = as_vec8<E>(lds_b128(vt, rops.off(32 * mb, 0)));
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 qv = u32x4{0, 0, 0, 0}, gv = u32x4{0, 0, 0, 0};
+      if (qi < nq) {
+        qv = *(const u32x4*)(Qp + (size_t)qi * D + 16 * kk + 8 * h32);
+        gv = *(const u32x4*)(Gp + (size_t)qi * D + 16 * kk + 8 * h32);
       }
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        if (kk + 1 < KS) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            ka[(kk + 1) & 1][mb] = as_vec8<E>(lds_b128(kt, rops.off(32 * mb, kk + 1)));
-            va[(kk + 1) & 1][mb] = as_vec8<E>(lds_b128(vt, rops.off(32 * mb, kk + 1)));
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          sc[mb] = E::mfma32(ka[kk & 1][mb], qreg[kk], sc[mb]);
-          dp[mb] = E::mfma32(va[kk & 1][mb], greg[kk], dp[mb]);
-        }
-      }
-      uint32_t gw[2][8];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int jj = j0 + 32 * mb + 8 * g4 + 4 * h32;
-          unsigned allow = 0xFu, keep = 0xFu;
-          if (cls == kPartial) allow = allowed4<MK>(a.mask, q, jj, nq, nk, cbm);
-          if constexpr (DROP) keep = keep4(a.drop, bh, q, jj);
-          float gm[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = fast_exp2(fmaf(sc[mb][4 * g4 + r], sl2, -lse2));
-            float dpv = dp[mb][4 * g4 + r];
-            if constexpr (DROP) dpv = ((keep >> r) & 1u) ? dpv * a.drop.inv_keep : 0.f;
-            gm[r] = ((allow >> r) & 1u) ? pv * (dpv - dval) : 0.f;
-          }
-          gw[mb][2 * g4] = E::pack2(gm[0], gm[1]);
-          gw[mb][2 * g4 + 1] = E::pack2(gm[2], gm[3]);
-        }
-      // dQ^T += K^T gamma^T (K^T operands read one step ahead)
-      vec8 gbs[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int mb = ks >> 1, o = (ks & 1) * 4;
-        gbs[ks] = as_vec8<E>(u32x4{gw[mb][o], gw[mb][o + 1], gw[mb][o + 2], gw[mb][o + 3]});
-      }
-      constexpr int NT = 4 * MD;
-      vec8 kta[2];
-      kta[0] = as_vec8<E>(tops.read(kt, 0, 0));
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int ks = t / MD, md = t % MD;
-        if (t + 1 < NT) kta[(t + 1) & 1] = as_vec8<E>(tops.read(kt, 16 * ((t + 1) / MD), (t + 1) % MD));
-        dq[md] = E::mfma32(kta[t & 1], gbs[ks], dq[md]);
-      }
+      qreg[kk] = as_vec8<E>(qv);
+      greg[kk] = as_vec8<E>(gv);
     }
-
-    wait_vm();
-    __syncthreads();
-    stage ^= 1;
-    jt = nxt;
-  }
-
-  if (q < nq) {
-    uint16_t* dQp = (uint16_t*)a.dQ + (size_t)bh * nq * D + (size_t)q * D;
-    const float c = a.scale;
+    const float lse2 = (qi < nq) ? a.Lws[(size_t)bh * nq + qi] : __builtin_huge_valf();
+    const float dval = (qi < nq) ? a.Dws[(size_t)bh * nq + qi] : 0.f;
+    f32x16 dq[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int col = 32 * md + 8 * g4 + 4 * h32;
-        u32x2 w;
-        w[0] = E::pack2(dq[md][4 * g4] * c, dq[md][4 * g4 + 1] * c);
-        w[1] = E::pack2(dq[md][4 * g4 + 2] * c, dq[md][4 * g4 + 3] * c);
-        *(u32x2*)(dQp + col) = w;
+      for (int r2 = 0; r2 < 16; ++r2) dq[md][r2] = 0.f;
+
+    const int qlast = min(q0 + BQ, nq) - 1;
+    int jt_lo = 0, jt_hi = (nk - 1) / BK;
+    if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
+    if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
+    auto wg_nonempty = [&](int jt) {
+      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
+    };
+    auto next_of = [&](int jt) {
+      for (++jt; jt <= jt_hi; ++jt)
+        if (MK == kArith || wg_nonempty(jt)) return jt;
+      return -1;
+    };
+    auto copy_one = [&](int jt, auto st, int u) __attribute__((always_inline)) {
+      if (u < PW) tcopy.issue_one(kbuf(st), Krs, jt * BK, nk - 1, u);
+      else tcopy.issue_one(vbuf(st), Vrs, jt * BK, nk - 1, u - PW);
+    };
+    // operand t: A(mb) slots alternate K rows (S^T) and V rows (dP^T) per
+    // k-step; B(mb) slots read K^T for (16-key step kh, md)
+    auto operand = [&](auto st, int t) __attribute__((always_inline)) {
+      if (t < 2 * NA) {
+        const int mb = t / NA, u = t % NA, kk = u / 2;
+        return as_vec8<E>(lds_b128((u & 1) ? vbuf(st) : kbuf(st), rops.off(32 * mb, kk)));
       }
+      const int u = t - 2 * NA, mb = u / NB, kh = (u % NB) / MD, md = u % MD;
+      return as_vec8<E>(tops.read(kbuf(st), 32 * mb + 16 * kh, md));
+    };
+    // key interval of this lane's row for arithmetic masks: key base + c is
+    // allowed iff (unsigned)(c - lo) <= rng
+    auto arith_interval = [&](int base, int& lo, unsigned& rng) __attribute__((always_inline)) {
+      int jlo = 0, jhi = nk - 1;
+      if (a.mask.causal) jhi = min(jhi, qi);
+      if (a.mask.window > 0) jlo = max(jlo, qi - a.mask.window + 1);
+      const bool any = qi < nq && jlo <= jhi;
+      lo = any ? jlo - base : (1 << 24);
+      rng = any ? (unsigned)(jhi - jlo) : 0u;
+    };
+    struct Gam {
+      uint32_t gw[8];
+      unsigned allow[4], keep[4];
+    };
+    // sub-part k = 2 g4 + half of W(mb): keys key0 + 8 g4 + 4 h32 + 2 half + e
+    auto weights = [&](Gam& w, const f32x16& sc, const f32x16& dp, int k, int key0, auto part_tag, bool cbm)
+                       __attribute__((always_inline)) {
+      constexpr bool PART = decltype(part_tag)::value;
+      const int g4 = k / 2, half = k % 2;
+      const int jj = key0 + 8 * g4 + 4 * h32;
+      if (half == 0) {
+        w.allow[g4] = 0xFu;
+        w.keep[g4] = 0xFu;
+        if constexpr (PART) {
+          if constexpr (MK == kArith) {
+            int lo;
+            unsigned rng;
+            arith_interval(jj, lo, rng);
+            unsigned al = 0;
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) al |= ((unsigned)(r2 - lo) <= rng ? 1u : 0u) << r2;
+            w.allow[g4] = al;
+          } else {
+            w.allow[g4] = allowed4<MK>(a.mask, qi, jj, nq, nk, cbm);
+          }
+        }
+        if constexpr (DROP) w.keep[g4] = keep4(a.drop, bh, qi, jj);
+      }
+      float gm[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r2 = 2 * half + e;
+        const float pv = fast_exp2(fmaf(sc[4 * g4 + r2], sl2, -lse2));
+        float dpv = dp[4 * g4 + r2];
+        if constexpr (DROP) dpv = ((w.keep[g4] >> r2) & 1u) ? dpv * a.drop.inv_keep : 0.f;
+        const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
+        gm[e] = al ? pv * (dpv - dval) : 0.f;
+      }
+      w.gw[2 * g4 + half] = E::pack2(gm[0], gm[1]);
+      materialize(w.gw[2 * g4 + half]);
+    };
+    auto pack_op = [&](const uint32_t (&x)[8], int kh) __attribute__((always_inline)) {
+      return as_vec8<E>(u32x4{x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]});
+    };
+
+    auto tile = [&](auto st, int jt, int jn, auto part_tag, bool cbm) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
+      const int j0 = jt * BK;
+      f32x16 sc[2], dp[2];
+      Gam w[2];
+      vec8 opb[3];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) opb[k] = operand(st, k);
+      static_for<NSLOT>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (t + 2 < NSLOT) opb[(t + 2) % 3] = operand(st, t + 2);
+        const vec8 op = opb[t % 3];
+        if constexpr (t < 2 * NA) {
+          constexpr int mb = t / NA, u = t % NA, kk = u / 2;
+          if constexpr (u == 0) {
+#pragma unroll
+            for (int r2 = 0; r2 < 16; ++r2) { sc[mb][r2] = 0.f; dp[mb][r2] = 0.f; }
+          }
+          if constexpr (u & 1) dp[mb] = E::mfma32(op, greg[kk], dp[mb]);
+          else sc[mb] = E::mfma32(op, qreg[kk], sc[mb]);
+          if constexpr (mb == 0) {  // the copy of the next tile
+            static_for<NCOPY>([&](auto uc) __attribute__((always_inline)) {
+              constexpr int cu = decltype(uc)::value;
+              if constexpr ((cu * NA) / NCOPY == u) copy_one(jn, Next{}, cu);
+            });
+          } else {  // W(0) under A(1)
+            static_for<8>([&](auto kc) __attribute__((always_inline)) {
+              constexpr int k = decltype(kc)::value;
+              if constexpr ((k * NA) / 8 == u) weights(w[0], sc[0], dp[0], k, j0, part_tag, cbm);
+            });
+          }
+        } else {
+          constexpr int u = t - 2 * NA, mb = u / NB, kh = (u % NB) / MD, md = u % MD;
+          dq[md] = E::mfma32(op, pack_op(w[mb].gw, kh), dq[md]);
+          if constexpr (mb == 0) {  // W(1) under B(0)
+            static_for<8>([&](auto kc) __attribute__((always_inline)) {
+              constexpr int k = decltype(kc)::value;
+              if constexpr ((k * NB) / 8 == u) weights(w[1], sc[1], dp[1], k, j0 + 32, part_tag, cbm);
+            });
+          }
+        }
+        ETS_FENCE();
+      });
+    };
+    auto empty_tile = [&](auto st, int jn) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(jn, Next{}, u);
+    };
+    auto finish = [&]() __attribute__((always_inline)) {
+      wait_vm();
+      __syncthreads();
+    };
+    auto general_step = [&](auto st, int jt, int jn) __attribute__((always_inline)) {
+      const int j0 = jt * BK;
+      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nq, nk);
+      const int cls = cinfo & kClassMask;
+      if (cls == kFull) tile(st, jt, jn, std::false_type{}, false);
+      else if (cls == kPartial) tile(st, jt, jn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      else empty_tile(st, jn);
+      finish();
+    };
+
+    int jt = -1;
+    if (jt_lo <= jt_hi) jt = (MK == kArith || wg_nonempty(jt_lo)) ? jt_lo : next_of(jt_lo);
+    if (jt >= 0) {
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(jt, Stage0{}, u);
+    }
+    finish();
+    for (int p = 0; jt >= 0; ++p) {
+      const int jn = next_of(jt);
+      if (p & 1) general_step(Stage1{}, jt, jn >= 0 ? jn : jt);
+      else general_step(Stage0{}, jt, jn >= 0 ? jn : jt);
+      jt = jn;
+    }
+
+    if (qi < nq) {
+      uint16_t* dQp = (uint16_t*)a.dQ + (size_t)bh * nq * D + (size_t)qi * D;
+      const float c = a.scale;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * md + 8 * g4 + 4 * h32;
+          u32x2 wv;
+          wv[0] = E::pack2(dq[md][4 * g4] * c, dq[md][4 * g4 + 1] * c);
+          wv[1] = E::pack2(dq[md][4 * g4 + 2] * c, dq[md][4 * g4 + 3] * c);
+          *(u32x2*)(dQp + col) = wv;
+        }
+    }
   }
 }
 
@@ -666,17 +745,27 @@ static int launch_dkdv(const DenseArgs& a, hipStream_t st) {
   return launch_dkdv_k<E, D, kDenseM, false>(a, st);
 }
 
+template <class E, int D, int MK, bool DROP>
+static int launch_dq_k(const DenseArgs& a, hipStream_t st) {
+  const int n_qtiles = (a.nq + 127) / 128;
+  const int n_items = n_qtiles * a.B * a.H;
+  int slots = 0;
+  ETS_TRY(resident_slots(dense_bwd_dq_kernel<E, D, MK, DROP>, 256, &slots));
+  ETS_TRY(launch((dense_bwd_dq_kernel<E, D, MK, DROP>), dim3(min(n_items, slots)), dim3(256), 0, st, a, n_qtiles));
+  return 0;
+}
+
 template <class E, int D>
-static hipError_t launch_dq(const DenseArgs& a, dim3 g, hipStream_t st, int n_qtiles) {
+static int launch_dq(const DenseArgs& a, hipStream_t st) {
   const int mk = mask_kind(a.mask);
   if (a.drop.enabled) {
-    if (mk == kArith) return launch((dense_bwd_dq_kernel<E, D, kArith, true>), g, dim3(256), 0, st, a, n_qtiles);
-    if (mk == kBlock) return launch((dense_bwd_dq_kernel<E, D, kBlock, true>), g, dim3(256), 0, st, a, n_qtiles);
-    return launch((dense_bwd_dq_kernel<E, D, kDenseM, true>), g, dim3(256), 0, st, a, n_qtiles);
+    if (mk == kArith) return launch_dq_k<E, D, kArith, true>(a, st);
+    if (mk == kBlock) return launch_dq_k<E, D, kBlock, true>(a, st);
+    return launch_dq_k<E, D, kDenseM, true>(a, st);
   }
-  if (mk == kArith) return launch((dense_bwd_dq_kernel<E, D, kArith, false>), g, dim3(256), 0, st, a, n_qtiles);
-  if (mk == kBlock) return launch((dense_bwd_dq_kernel<E, D, kBlock, false>), g, dim3(256), 0, st, a, n_qtiles);
-  return launch((dense_bwd_dq_kernel<E, D, kDenseM, false>), g, dim3(256), 0, st, a, n_qtiles);
+  if (mk == kArith) return launch_dq_k<E, D, kArith, false>(a, st);
+  if (mk == kBlock) return launch_dq_k<E, D, kBlock, false>(a, st);
+  return launch_dq_k<E, D, kDenseM, false>(a, st);
 }
 
 template <class E, int D>
@@ -687,13 +776,14 @@ static int launch_bwd_t(const DenseArgs& a, void* stream, int phases) {
     const int prep_threads = (rows + 64) * (D / 8);
     ETS_TRY(launch((dense_bwd_prep_kernel<E, D>), dim3((prep_threads + 255) / 256), dim3(256), 0, st, a, rows));
   }
-  const int n_qtiles = (a.nq + 127) / 128;
-  dim3 gq(n_qtiles * a.B * a.H);
   if (phases & 2) {
     const int rc = launch_dkdv<E, D>(a, st);
     if (rc) return rc;
   }
-  if (phases & 4) ETS_TRY((launch_dq<E, D>(a, gq, st, n_qtiles)));
+  if (phases & 4) {
+    const int rc = launch_dq<E, D>(a, st);
+    if (rc) return rc;
+  }
   return 0;
 }
 
