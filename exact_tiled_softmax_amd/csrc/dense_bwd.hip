@@ -433,12 +433,50 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
       for (int u = 0; u < NCOPY; ++u) copy_one(st, Stage0{}, u);
     }
     finish();
-    for (int p = 0; st >= 0; ++p) {
-      const int sn = next_of(st);
-      if (p & 1) general_step(Stage1{}, st, sn >= 0 ? sn : st);
-      else general_step(Stage0{}, st, sn >= 0 ? sn : st);
-      st = sn;
+    // Step number p runs on stage p % 2.  For arithmetic masks the query
+    // tiles that the whole key block sees whole form one range per head;
+    // pairs of them starting on stage 0 run without classification in a loop
+    // of their own (one code path, so the accumulators stay in place).
+    int p = 0;
+    auto general_until = [&](int st_end) __attribute__((always_inline)) {
+      while (st >= 0 && st < st_end) {
+        const int sn = next_of(st);
+        if (p & 1) general_step(Stage1{}, st, sn >= 0 ? sn : st);
+        else general_step(Stage0{}, st, sn >= 0 ? sn : st);
+        st = sn;
+        ++p;
+      }
+    };
+    if constexpr (MK == kArith) {
+      // local q-tile indices i (qb0 = (qt_lo + i) BQ) whose rows see all 128 keys
+      int i_lo = 0, i_hi = n_qt - 1;
+      if (k0 + 127 >= nk) i_hi = -1;
+      i_hi = min(i_hi, (nq - BQ) / BQ - qt_lo);
+      if (a.mask.causal) i_lo = max(i_lo, (k0 + 127 + BQ - 1) / BQ - qt_lo);
+      if (a.mask.window > 0) {
+        const int lim = k0 + a.mask.window - BQ;  // full iff qb0 <= lim
+        i_hi = (lim < 0) ? -1 : min(i_hi, lim / BQ - qt_lo);
+      }
+      for (int hi = 0; hi < grp && i_lo <= i_hi; ++hi) {
+        int a0 = hi * n_qt + i_lo, a1 = hi * n_qt + i_hi + 1;
+        general_until(a0);
+        if (st != a0) break;  // (not reached: arithmetic masks skip no step)
+        if (p & 1) {
+          general_until(a0 + 1);
+          ++a0;
+        }
+        if ((a1 - a0) & 1) --a1;
+        for (; st < a1; st += 2, p += 2) {
+          step(Stage0{}, st, st + 1, std::false_type{}, false);
+          finish();
+          const int sn = next_of(st + 1);
+          step(Stage1{}, st + 1, sn >= 0 ? sn : st + 1, std::false_type{}, false);
+          finish();
+        }
+        if (st >= total) st = -1;
+      }
     }
+    general_until(1 << 30);
 
     // ---- epilogue: dK = c dK^T, dV = (1/(1-rho)) dV^T; lane holds one key
     if (key < nk) {
