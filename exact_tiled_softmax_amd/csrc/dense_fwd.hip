@@ -39,7 +39,7 @@ namespace ets {
 constexpr float kRescaleSlack = 8.0f;
 
 template <class E, int D, int NW, int MK, bool DROP>
-__global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2) void dense_fwd_kernel(const DenseArgs a, int n_qtiles) {
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dense_fwd_kernel(const DenseArgs a, int n_qtiles) {
   constexpr int BK = 64;
   constexpr int BQ = NW * 32;
   constexpr int KS = D / 16;        // k-steps of the score contraction

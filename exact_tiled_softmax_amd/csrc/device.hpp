@@ -7,6 +7,7 @@
 #include <tuple>
 #include <type_traits>
 #include <utility>
+#include <mutex>
 
 #include "params.hpp"
 
@@ -41,26 +42,40 @@ inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds
 }
 
 // Workgroups of `kernel` that the device keeps resident at once (compute
-// units x workgroups per unit), cached per device.  Persistent kernels launch
-// at most this many workgroups.
-template <class... P>
-inline hipError_t resident_slots(void (*kernel)(P...), int block_threads, int* slots) {
-  static int cache[64] = {0};
+// units x workgroups per unit), cached per (kernel, device).  Persistent
+// kernels launch at most this many workgroups.
+inline hipError_t resident_slots_fn(const void* fn, int block_threads, int* slots) {
+  struct Entry {
+    const void* fn;
+    int dev, slots;
+  };
+  static std::mutex mu;
+  static Entry cache[256];
+  static int n = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *slots = cache[dev];
-    return hipSuccess;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; ++i)
+      if (cache[i].fn == fn && cache[i].dev == dev) {
+        *slots = cache[i].slots;
+        return hipSuccess;
+      }
   }
   int per_cu = 0, cus = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, block_threads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block_threads, 0);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   *slots = per_cu > 0 && cus > 0 ? per_cu * cus : 1;
-  if (dev >= 0 && dev < 64) cache[dev] = *slots;
+  std::lock_guard<std::mutex> lock(mu);
+  if (n < 256) cache[n++] = Entry{fn, dev, *slots};
   return hipSuccess;
+}
+template <class... P>
+inline hipError_t resident_slots(void (*kernel)(P...), int block_threads, int* slots) {
+  return resident_slots_fn((const void*)kernel, block_threads, slots);
 }
 
 #define ETS_TRY(expr)                      \
