@@ -735,12 +735,49 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       for (int u = 0; u < NCOPY; ++u) copy_one(jt, Stage0{}, u);
     }
     finish();
-    for (int p = 0; jt >= 0; ++p) {
-      const int jn = next_of(jt);
-      if (p & 1) general_step(Stage1{}, jt, jn >= 0 ? jn : jt);
-      else general_step(Stage0{}, jt, jn >= 0 ? jn : jt);
-      jt = jn;
+    // Tile number p runs on stage p % 2.  For arithmetic masks the tiles
+    // every row of the workgroup sees whole form one range; pairs of them
+    // starting on stage 0 run in a loop of their own (one code path, so the
+    // accumulators stay in place).
+    int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
+    if constexpr (MK == kArith) {
+      if (q0 + BQ <= nq) {
+        int f_lo = jt_lo, f_hi = min(jt_hi, nk / BK - 1);
+        if (a.mask.causal) f_hi = min(f_hi, q0 >= BK - 1 ? (q0 - (BK - 1)) / BK : -1);
+        if (a.mask.window > 0) {
+          const int t = q0 + BQ - 1 - a.mask.window;  // full iff j0 > t
+          if (t >= 0) f_lo = max(f_lo, t / BK + 1);
+        }
+        if (f_lo <= f_hi) {
+          const int lo = f_lo - jt_lo, hi = f_hi - jt_lo + 1;
+          const int p0 = lo + (lo & 1), p1 = hi - ((hi - p0) & 1);
+          if (p0 < p1) { fp0 = p0; fp1 = p1; }
+        }
+      }
     }
+    int p = 0;
+    auto general_run = [&](int p_end) __attribute__((always_inline)) {
+      for (; jt >= 0 && p < p_end; ++p) {
+        const int jn = next_of(jt);
+        if (p & 1) general_step(Stage1{}, jt, jn >= 0 ? jn : jt);
+        else general_step(Stage0{}, jt, jn >= 0 ? jn : jt);
+        jt = jn;
+      }
+    };
+    general_run(fp0);
+    if (fp0 < fp1) {
+      // general_run stopped at tile number fp0 < N: jt = jt_lo + p, and
+      // tile p + 1 is whole too
+      for (; p < fp1; p += 2) {
+        tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
+        finish();
+        const int jn = next_of(jt + 1);
+        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, std::false_type{}, false);
+        finish();
+        jt = jn;
+      }
+    }
+    general_run(1 << 30);
 
     if (qi < nq) {
       uint16_t* dQp = (uint16_t*)a.dQ + (size_t)bh * nq * D + (size_t)qi * D;
