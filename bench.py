@@ -94,6 +94,22 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "dispatches": 5}), flush=True)
 
 
+def mfma_microbench(waves_per_simd=2, iters=4096):
+    """Dense bf16 MFMA rate this device sustains (no memory traffic), TFLOP/s."""
+    import torch
+    import exact_tiled_softmax_amd as ets
+    sink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ets.attn_mfma_probe(waves_per_simd, 64, sink, sink.numel(), stream=stream)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n = ets.attn_mfma_probe(waves_per_simd, iters, sink, sink.numel(), stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tf = n * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"TFLOP/s": tf, "frac_of_datasheet": tf / PEAK_TFLOPS["bf16"], "waves_per_simd": waves_per_simd}
+
+
 def dense_pairs(w, block_mask):
     """|A| = number of allowed (query, key) pairs per (batch, head) lane, counted on the host."""
     n = w.n
@@ -151,6 +167,9 @@ def bench_dense(w, args):
     import exact_tiled_softmax_amd as ets
     from tests import gpu_helpers as gh
 
+    if args.no_dropout and w.rho > 0:
+        import dataclasses
+        w = dataclasses.replace(w, rho=0.0)
     arr = workloads.dense_arrays(w)
     block_mask = arr["block_mask"]
     dt = DTYPE_CODE[w.dtype]
@@ -227,6 +246,7 @@ def bench_dense(w, args):
         "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_tf, "frac_peak": bwd_tf / peak},
         "kernels": kernels,
         "roofline": roofline,
+        "mfma_microbench": mfma_microbench(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_dense(w, arr, block_mask)
@@ -333,6 +353,7 @@ def main():
     ap.add_argument("--workload", default="dense_causal_bf16_b4h16_n2048_d128", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only the reference copy (counter scaling)")
+    ap.add_argument("--no-dropout", action="store_true", help="dense workloads: run the same shape with rate 0")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -18,7 +18,7 @@ __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "AttnError", "Mask", "Dropout",
     "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
-    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_status_string", "library_path", "lib",
+    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_status_string", "library_path", "lib",
 ]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
@@ -92,6 +92,8 @@ lib.attn_sparse_bwd.restype = _i
 lib.attn_sparse_bwd.argtypes = ([_i] + [_i] * 6 + [_vp] * 5 + [_f] + [_vp] * 3 + [_vp] * 3 + [_vp, _sz, _vp])
 lib.attn_dropout_mask.restype = _i
 lib.attn_dropout_mask.argtypes = [_f, ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
+lib.attn_mfma_probe.restype = _i
+lib.attn_mfma_probe.argtypes = [_i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 
 
 class AttnError(RuntimeError):
@@ -202,3 +204,12 @@ def attn_sparse_bwd(dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_lengt
 def attn_dropout_mask(rate, seed, B, H, n_q, n_k, xi, stream=None, raise_on_error=True):
     st = lib.attn_dropout_mask(float(rate), int(seed), B, H, n_q, n_k, _ptr(xi), _stream(stream))
     return _check(st, "attn_dropout_mask", raise_on_error)
+
+
+def attn_mfma_probe(waves_per_simd, iters, sink, sink_len, stream=None, raise_on_error=True):
+    """Launch the MFMA-rate probe; returns the number of MFMA instructions issued."""
+    n = ctypes.c_longlong(0)
+    st = lib.attn_mfma_probe(int(waves_per_simd), int(iters), _ptr(sink), int(sink_len), ctypes.byref(n),
+                             _stream(stream))
+    _check(st, "attn_mfma_probe", raise_on_error)
+    return n.value

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "dense_fwd.hip", "dense_bwd.hip", "dense_f32.hip", "dropout.hip", "sparse.hip"]
+SOURCES = ["abi.cpp", "dense_fwd.hip", "dense_bwd.hip", "dense_f32.hip", "dropout.hip", "sparse.hip", "probe.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -252,4 +252,13 @@ attn_status attn_dropout_mask(float rate, uint64_t seed, int B, int H, int n_q, 
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_mfma_probe(int waves_per_simd, int iters, float* sink, int sink_len, long long* mfmas,
+                            void* stream) {
+  if ((waves_per_simd != 1 && waves_per_simd != 2) || iters < 1 || !sink || !mfmas || sink_len < 1)
+    return ATTN_ERR_INVALID_ARG;
+  const int rc = launch_mfma_probe(waves_per_simd, iters, sink, sink_len, mfmas, stream);
+  if (rc == -1) return ATTN_ERR_INVALID_ARG;  // sink shorter than the CU count
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -66,6 +66,7 @@ int launch_dense_bwd_f32(const DenseArgs& a, void* stream, int phases);
 int launch_sparse_fwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_sparse_bwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_dropout_mask(const DropArgs& d, int B, int H, int nq, int nk, uint8_t* xi, void* stream);
+int launch_mfma_probe(int waves_per_simd, int iters, float* sink, int sink_len, long long* mfmas, void* stream);
 
 // Shapes the MFMA kernels are built for.
 bool dense_mfma_supported(int d, int dv);

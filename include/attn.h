@@ -218,6 +218,20 @@ attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
 attn_status attn_dropout_mask(float rate, uint64_t seed, int B, int H, int n_q, int n_k,
                               uint8_t* xi, void* stream);
 
+/*
+ * attn_mfma_probe -- measurement aid, not part of the method: launches one
+ * workgroup of 4 * waves_per_simd waves (1 or 2) on every compute unit, each
+ * wave issuing iters x 8 dense bf16 v_mfma_f32_32x32x16 with no memory
+ * traffic, so that the caller can time the launch and report the MFMA rate
+ * the device sustains beside the datasheet peak.  sink: device float buffer of
+ * sink_len >= number of compute units (receives one value per workgroup).
+ * *mfmas (host) receives the number of MFMA instructions issued
+ * (32x32x16x2 = 32768 flops each).  INVALID_ARG for waves_per_simd outside
+ * {1, 2}, iters < 1, null pointers or a sink shorter than the CU count.
+ */
+attn_status attn_mfma_probe(int waves_per_simd, int iters, float* sink, int sink_len, long long* mfmas,
+                            void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(attn_status status);
 

@@ -112,6 +112,15 @@ def test_dropout_mask_rejects_bad_rate():
     assert ets.attn_dropout_mask(0.1, 0, 1, 1, 4, 4, None, stream=0, raise_on_error=False) == ets.ATTN_ERR_INVALID_ARG
 
 
+def test_mfma_probe_rejects_bad_arguments():
+    import ctypes
+    import exact_tiled_softmax_amd as ets
+    for w, it, sink, n in ((3, 10, P, 256), (1, 0, P, 256), (1, 10, None, 256), (2, 10, P, 0)):
+        cnt = ctypes.c_longlong(0)
+        st = ets.lib.attn_mfma_probe(w, it, ets._ptr(sink), n, ctypes.byref(cnt), None)
+        assert st == ets.ATTN_ERR_INVALID_ARG
+
+
 def test_one_hip_runtime_per_process():
     # the library binds to the HIP runtime PyTorch loads, whatever the import order
     code = ("import exact_tiled_softmax_amd, torch\n"

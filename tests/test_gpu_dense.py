@@ -248,3 +248,14 @@ def test_invalid_arguments_touch_nothing():
         assert st == case["code"], case
     torch.cuda.synchronize()
     assert bool((Y == 123).all()) and bool((LSE == 5.0).all())
+
+
+def test_mfma_probe_runs_and_counts():
+    import exact_tiled_softmax_amd as ets
+    torch = gh.torch_cuda()
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    n = ets.attn_mfma_probe(2, 8, sink, sink.numel())
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert n == cus * 8 * 8 * 8
+    assert bool(torch.isfinite(sink[:cus]).all())
