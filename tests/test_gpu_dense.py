@@ -138,6 +138,17 @@ def test_window_and_block_mask(dtype, d):
     _assert_close(r, ref, dtype)
 
 
+@pytest.mark.parametrize("causal,window,n,d", [(True, 300, 700, 128), (False, 200, 520, 64), (True, 64, 640, 128)])
+def test_window_only_long_enough_for_whole_tiles(causal, window, n, d):
+    # arithmetic masks long enough that every kernel has runs of tiles (and of
+    # dK/dV steps) that every row of a workgroup sees whole, with ragged ends
+    a = _inputs(1, 2, 2, n, d, d, "bf16", 80 + d)
+    c = 1.0 / math.sqrt(d)
+    r = gh.dense_run("bf16", a["Q"], a["K"], a["V"], a["G"], gh.mask_arg(causal=causal, window=window), c)
+    ref = _oracle(a, dense.Allowed(n, n, causal=causal, window=window), c)
+    _assert_close(r, ref, "bf16", f"causal={causal} window={window} n={n}")
+
+
 def test_dense_mask_with_empty_leading_blocks_and_empty_rows():
     n, d = 130, 64
     a = _inputs(1, 2, 2, n, d, d, "bf16", 30)
@@ -154,9 +165,9 @@ def test_dense_mask_with_empty_leading_blocks_and_empty_rows():
     assert np.all(np.isneginf(r["LSE"][:, :, [3, 77, 129]]))
 
 
-@pytest.mark.parametrize("H,H_kv", [(4, 2), (4, 1)])
-def test_grouped_heads(H, H_kv):
-    n, d = 200, 128
+@pytest.mark.parametrize("H,H_kv,n", [(4, 2, 200), (4, 1, 200), (4, 2, 530)])
+def test_grouped_heads(H, H_kv, n):
+    d = 128
     a = _inputs(2, H, H_kv, n, d, d, "bf16", 40 + H_kv)
     c = 1.0 / math.sqrt(d)
     r = gh.dense_run("bf16", a["Q"], a["K"], a["V"], a["G"], gh.mask_arg(causal=True), c)
