@@ -72,7 +72,7 @@ void fill_dense(DenseArgs& a, attn_dtype dt, int B, int H, int H_kv, int n_q, in
   if (drop && drop->rate > 0.f) {
     const double r = (double)drop->rate;
     a.drop.enabled = 1;
-    a.drop.threshold = (uint32_t)std::floor(r * 4294967296.0);
+    a.drop.threshold = (uint32_t)std::floor(r * 65536.0);
     a.drop.seed_lo = (uint32_t)(drop->seed & 0xffffffffu);
     a.drop.seed_hi = (uint32_t)(drop->seed >> 32);
     a.drop.inv_keep = (float)(1.0 / (1.0 - r));

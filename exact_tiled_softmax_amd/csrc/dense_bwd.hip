@@ -59,20 +59,27 @@ __global__ __launch_bounds__(256) void dense_bwd_prep_kernel(const DenseArgs a, 
   }
 }
 
-// Keep bits (4 query rows i0..i0+3, this lane's key j) for the key-major
-// layout.  The four lanes of a quad hold keys 4k..4k+3; lane u of the quad
-// draws the Philox block of query row i0 + u (which decides all four keys) and
-// the quad exchanges the decisions, so each block is drawn exactly once.
-__device__ __forceinline__ unsigned keep4_rows(const DropArgs& d, int lane_bh, int i0, int j) {
-  const int u = j & 3;
-  const unsigned nib = keep4(d, lane_bh, i0 + u, j & ~3);
-  int v = (int)(nib << (4 * u));
-  v |= __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  v |= __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  unsigned out = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) out |= (((unsigned)v >> (4 * r + u)) & 1u) << r;
-  return out;
+// Keep bits for the key-major layout, where the eight lanes of an octet hold
+// the keys 8k .. 8k+7 of one 8-key Philox block (lane u holds key 8k + u) and
+// share their query rows: rows i0 .. i0+3 (out0) and i0+8 .. i0+11 (out1).
+// Lane u draws the block of row i0 + u (u < 4) or i0 + 4 + u (u >= 4), the
+// octet ORs the eight draws together, and each lane keeps its key's bit of
+// every row: bit 8 r of out0 (out1) keeps row i0 + r (i0 + 8 + r).  Each
+// block is drawn exactly once.
+__device__ __forceinline__ void keep8_rows(const DropArgs& d, int lane_bh, int i0, int j, unsigned& out0,
+                                           unsigned& out1) {
+  const int u = j & 7;
+  const unsigned blk = keep8(d, lane_bh, i0 + (u < 4 ? u : 4 + u), j & ~7);
+  int lo = u < 4 ? (int)(blk << (8 * u)) : 0;
+  int hi = u < 4 ? 0 : (int)(blk << (8 * (u - 4)));
+  lo |= __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  hi |= __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false);
+  lo |= __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  hi |= __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false);
+  lo |= __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, false);  // row_half_mirror: the other quad
+  hi |= __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, false);
+  out0 = ((unsigned)lo >> u) & 0x01010101u;
+  out1 = ((unsigned)hi >> u) & 0x01010101u;
 }
 
 // --------------------------------------------------------------------- dK, dV
@@ -305,7 +312,6 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
       const int qr = 32 * mq + 8 * g4 + 4 * h32;
       if (half == 0) {
         w.allow[g4] = 0xFu;
-        w.keep[g4] = 0xFu;
         if constexpr (PART) {
           if constexpr (MK == kArith) {
             int lo;
@@ -319,7 +325,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
             w.allow[g4] = allowed4_rows<MK>(a.mask, qb0 + qr, key, nq, nk, cbm);
           }
         }
-        if constexpr (DROP) w.keep[g4] = keep4_rows(a.drop, lane_bh, qb0 + qr, key);
+        if constexpr (DROP)
+          if (g4 % 2 == 0) keep8_rows(a.drop, lane_bh, qb0 + qr, key, w.keep[g4], w.keep[g4 + 1]);
       }
       float pk[2], gm[2];
 #pragma unroll
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         float dpv = dp[4 * g4 + r2];
         bool kp = true;
         if constexpr (DROP) {
-          kp = (w.keep[g4] >> r2) & 1u;
+          kp = (w.keep[g4] >> (8 * r2)) & 1u;
           dpv = kp ? dpv * a.drop.inv_keep : 0.f;
         }
         const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
@@ -622,7 +629,8 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
     };
     struct Gam {
       uint32_t gw[8];
-      unsigned allow[4], keep[4];
+      unsigned allow[4];
+      unsigned keep;  // dropout: bit 8 g4 + r keeps key key0 + 8 g4 + 4 h32 + r
     };
     // sub-part k = 2 g4 + half of W(mb): keys key0 + 8 g4 + 4 h32 + 2 half + e
     auto weights = [&](Gam& w, const f32x16& sc, const f32x16& dp, int k, int key0, auto part_tag, bool cbm)
@@ -632,7 +640,6 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       const int jj = key0 + 8 * g4 + 4 * h32;
       if (half == 0) {
         w.allow[g4] = 0xFu;
-        w.keep[g4] = 0xFu;
         if constexpr (PART) {
           if constexpr (MK == kArith) {
             int lo;
@@ -646,7 +653,6 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
             w.allow[g4] = allowed4<MK>(a.mask, qi, jj, nq, nk, cbm);
           }
         }
-        if constexpr (DROP) w.keep[g4] = keep4(a.drop, bh, qi, jj);
       }
       float gm[2];
 #pragma unroll
@@ -654,7 +660,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
         const int r2 = 2 * half + e;
         const float pv = fast_exp2(fmaf(sc[4 * g4 + r2], sl2, -lse2));
         float dpv = dp[4 * g4 + r2];
-        if constexpr (DROP) dpv = ((w.keep[g4] >> r2) & 1u) ? dpv * a.drop.inv_keep : 0.f;
+        if constexpr (DROP) dpv = ((w.keep >> (8 * g4 + r2)) & 1u) ? dpv * a.drop.inv_keep : 0.f;
         const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
         gm[e] = al ? pv * (dpv - dval) : 0.f;
       }
@@ -670,6 +676,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       const int j0 = jt * BK;
       f32x16 sc[2], dp[2];
       Gam w[2];
+      unsigned kd[4];  // dropout draws of the tile's four blocks of 8 keys per lane pair
       vec8 opb[3];
 #pragma unroll
       for (int k = 0; k < 2; ++k) opb[k] = operand(st, k);
@@ -685,11 +692,20 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
           }
           if constexpr (u & 1) dp[mb] = E::mfma32(op, greg[kk], dp[mb]);
           else sc[mb] = E::mfma32(op, qreg[kk], sc[mb]);
-          if constexpr (mb == 0) {  // the copy of the next tile
+          if constexpr (mb == 0) {  // the copy of the next tile and the dropout keep bits
             static_for<NCOPY>([&](auto uc) __attribute__((always_inline)) {
               constexpr int cu = decltype(uc)::value;
               if constexpr ((cu * NA) / NCOPY == u) copy_one(jn, Next{}, cu);
             });
+            if constexpr (DROP) {
+              static_for<4>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr ((q * NA) / 4 == u) {
+                  kd[q] = keep_qm_draw(a.drop, bh, qi, j0 + 32 * (q / 2), h32, q % 2);
+                  if constexpr (q % 2 == 1) w[q / 2].keep = keep_qm_merge(kd[q - 1], kd[q], h32);
+                }
+              });
+            }
           } else {  // W(0) under A(1)
             static_for<8>([&](auto kc) __attribute__((always_inline)) {
               constexpr int k = decltype(kc)::value;

@@ -19,7 +19,7 @@ namespace ets {
 
 __device__ __forceinline__ float kappa1(const DropArgs& d, int lane_bh, int i, int j) {
   if (!d.enabled) return 1.f;
-  return ((keep4(d, lane_bh, i, j & ~3) >> (j & 3)) & 1u) ? d.inv_keep : 0.f;
+  return ((keep8(d, lane_bh, i, j & ~7) >> (j & 7)) & 1u) ? d.inv_keep : 0.f;
 }
 
 template <int DM>

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       float mx, alpha, mneg;
       bool need;
       uint32_t packed[8];
+      unsigned keep;  // dropout: bit 8 g4 + r keeps key key0 + 8 g4 + 4 h32 + r
     };
     // allowed keys of this lane's row form one interval for arithmetic masks:
     // key0 + c allowed iff lo <= c <= lo + rng (unsigned compare of c - lo)
@@ -207,10 +208,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
   #pragma unroll
         for (int r = 0; r < 4; ++r) lsum += p[r];  // the normaliser counts dropped weights too
         if constexpr (DROP) {
-          const unsigned keep = keep4(a.drop, bh, qi, key0 + 8 * g4 + 4 * h32);
   #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (!((keep >> r) & 1u)) p[r] = 0.f;
+            if (!((st.keep >> (8 * g4 + r)) & 1u)) p[r] = 0.f;
         }
         st.packed[2 * g4] = E::pack2(p[0], p[1]);
         st.packed[2 * g4 + 1] = E::pack2(p[2], p[3]);
@@ -249,6 +249,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
   #pragma unroll
       for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
       Summary sm0, sm1;
+      unsigned kd[4];  // dropout draws of the tile's four blocks of 8 keys per lane pair
       vec8 opb[3];
       opb[0] = operand(kt, vt, 0);
       opb[1] = operand(kt, vt, 1);
@@ -262,6 +263,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
             constexpr int u = decltype(uc)::value;
             if constexpr ((u * KS) / NCOPY == t) copy_one(jnext, Next{}, u);
           });
+          if constexpr (DROP) {  // the keep bits of both halves, before their summaries
+            static_for<4>([&](auto qc) __attribute__((always_inline)) {
+              constexpr int q = decltype(qc)::value;
+              if constexpr ((q * KS) / 4 == t) {
+                kd[q] = keep_qm_draw(a.drop, bh, qi, j0 + 32 * (q / 2), h32, q % 2);
+                if constexpr (q == 1) sm0.keep = keep_qm_merge(kd[0], kd[1], h32);
+                if constexpr (q == 3) sm1.keep = keep_qm_merge(kd[2], kd[3], h32);
+              }
+            });
+          }
         } else if constexpr (t < 2 * KS) {
           s1 = E::mfma32(op, qreg[t - KS], s1);
           static_for<7>([&](auto pc) __attribute__((always_inline)) {

@@ -402,12 +402,35 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
   return {c0, c1, c2, c3};
 }
 
-// Keep bits of dropout for keys j0 .. j0+3 (j0 % 4 == 0) of query row i in
-// lane (b*H + h): counter (j0/4, i, lane, 0), word r decides key j0 + r.
-__device__ __forceinline__ unsigned keep4(const DropArgs& d, int lane_bh, int i, int j0) {
-  U4 w = philox4x32_10((uint32_t)(j0 >> 2), (uint32_t)i, (uint32_t)lane_bh, 0u, d.seed_lo, d.seed_hi);
-  return (unsigned)(w.x >= d.threshold) | ((unsigned)(w.y >= d.threshold) << 1) |
-         ((unsigned)(w.z >= d.threshold) << 2) | ((unsigned)(w.w >= d.threshold) << 3);
+// Keep bits of dropout for keys j0 .. j0+7 (j0 % 8 == 0) of query row i in
+// lane (b*H + h): counter (j0/8, i, lane, 0); key j0 + e is decided by the
+// 16-bit half (e mod 2) of word e/2 (low half for even e), kept iff that half
+// is >= threshold.  Bit e of the result is key j0 + e.
+__device__ __forceinline__ unsigned keep8(const DropArgs& d, int lane_bh, int i, int j0) {
+  const U4 w = philox4x32_10((uint32_t)(j0 >> 3), (uint32_t)i, (uint32_t)lane_bh, 0u, d.seed_lo, d.seed_hi);
+  const uint32_t t = d.threshold;
+  auto two = [t](uint32_t x) __attribute__((always_inline)) {
+    return (unsigned)((x & 0xFFFFu) >= t) | ((unsigned)((x >> 16) >= t) << 1);
+  };
+  return two(w.x) | (two(w.y) << 2) | (two(w.z) << 4) | (two(w.w) << 6);
+}
+
+// Query-major layout (a lane of half h32 = lane / 32 holds keys
+// key0 + 8 g4 + 4 h32 + r, g4, r < 4, of one query row; lanes l and l ^ 32
+// hold the same row).  Each lane of the pair draws two of the four 8-key
+// blocks of the 32 keys, block 2 h32 + p on call p ...
+__device__ __forceinline__ unsigned keep_qm_draw(const DropArgs& d, int lane_bh, int i, int key0, int h32, int p) {
+  return keep8(d, lane_bh, i, key0 + 8 * (2 * h32 + p));
+}
+// ... and the pair swaps them: bit 8 g4 + r of the result keeps key
+// key0 + 8 g4 + 4 h32 + r.
+__device__ __forceinline__ unsigned keep_qm_merge(unsigned b0, unsigned b1, int h32) {
+  const uint32_t own = b0 | (b1 << 8);
+  const auto r = __builtin_amdgcn_permlane32_swap(own, own, false, false);
+  // r[0]: lanes 0-31 their own blocks 0, 1, lanes 32-63 their partner's;
+  // r[1]: lanes 0-31 the partner's blocks 2, 3, lanes 32-63 their own
+  const uint32_t all = (uint32_t)r[0] | ((uint32_t)r[1] << 16);  // byte b = block b
+  return (all >> (4 * h32)) & 0x0F0F0F0Fu;
 }
 
 // ------------------------------------------------------------ allowed sets

@@ -18,10 +18,10 @@ struct MaskArgs {
   const uint8_t* dense_mask;  // [nq][nk] or null
 };
 
-// Inverted dropout: keep iff Philox word >= threshold.
+// Inverted dropout: keep iff the key's 16-bit Philox draw >= threshold.
 struct DropArgs {
   int enabled;
-  uint32_t threshold;   // floor(rate * 2^32)
+  uint32_t threshold;   // floor(rate * 2^16)
   uint32_t seed_lo, seed_hi;
   float inv_keep;       // 1 / (1 - rate), fp32
 };

@@ -74,10 +74,11 @@ typedef struct {
  * Inverted dropout ([P2], "A different dropout mask changes the reverse
  * result"): each attention weight p_ij is multiplied by xi_ij / (1 - rate).
  * xi is regenerated, never stored: with Philox4x32-10 (Salmon et al., SC'11),
- * key = (seed mod 2^32, seed div 2^32) and counter = (j div 4, i, b*H + h, 0),
- * output word (j mod 4) is u and xi_ij = 0 iff u < floor(rate * 2^32), where
- * rate is widened to double.  The forward and reverse passes draw identical
- * xi.  The normaliser l_i and the LSE use the undropped weights.
+ * key = (seed mod 2^32, seed div 2^32) and counter = (j div 8, i, b*H + h, 0),
+ * u is the 16-bit half (j mod 2) of output word (j mod 8) div 2 (low half for
+ * even j) and xi_ij = 0 iff u < floor(rate * 2^16), where rate is widened to
+ * double: one draw decides eight keys.  The forward and reverse passes draw
+ * identical xi.  The normaliser l_i and the LSE use the undropped weights.
  * NULL or rate == 0: no dropout.  rate must lie in [0, 1).
  */
 typedef struct {

@@ -12,12 +12,15 @@ attention weight by xi/(1-rho) and must be replayed in the reverse pass
 do not say how xi is drawn; this library draws it from Philox4x32-10 with
 
   key     = (seed mod 2^32, seed div 2^32)
-  counter = (j div 4, i, b*H + h, 0)          (i = query row, j = key column)
-  u       = output word (j mod 4)
-  xi      = 0 if u < floor(rho * 2^32) else 1
+  counter = (j div 8, i, b*H + h, 0)          (i = query row, j = key column)
+  u       = 16-bit half (j mod 2) of output word (j mod 8) div 2
+            (the low half for even j, the high half for odd j)
+  xi      = 0 if u < floor(rho * 2^16) else 1
 
-so one Philox call covers four adjacent keys of one query row.  The GPU
-library implements the same written rule independently.
+so one Philox call covers eight adjacent keys of one query row, and the rate
+is resolved in steps of 2^-16 (at rho = 0.1 a weight is kept with probability
+1 - 6553/65536).  The GPU library implements the same written rule
+independently.
 
 PARITY: pinned at test time against an independent Philox4x32-10 (PyTorch's
 header-only C++ engine, compiled by the test), and on the GPU bit for bit.
@@ -58,10 +61,10 @@ def philox4x32_10(counter, key):
 
 
 def drop_threshold(rho):
-    """Integer threshold floor(rho * 2^32): a 32-bit word below it drops the weight."""
+    """Integer threshold floor(rho * 2^16): a 16-bit draw below it drops the weight."""
     if not (0.0 <= rho < 1.0):
         raise ValueError("dropout rate must lie in [0, 1)")
-    return int(np.floor(np.float64(rho) * 4294967296.0))
+    return int(np.floor(np.float64(rho) * 65536.0))
 
 
 def keep_mask(seed, rho, lane, rows, cols):
@@ -76,6 +79,8 @@ def keep_mask(seed, rho, lane, rows, cols):
     key = (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF)
     ii = rows[:, None]
     jj = cols[None, :]
-    x = philox4x32_10((jj // 4, ii, np.int64(lane), 0), key)
-    word = np.select([jj % 4 == 0, jj % 4 == 1, jj % 4 == 2], [x[0], x[1], x[2]], x[3])
-    return word.astype(np.uint64) >= np.uint64(thr)
+    x = philox4x32_10((jj // 8, ii, np.int64(lane), 0), key)
+    w = (jj % 8) // 2
+    word = np.select([w == 0, w == 1, w == 2], [x[0], x[1], x[2]], x[3]).astype(np.uint64)
+    u = np.where(jj % 2 == 0, word & np.uint64(0xFFFF), word >> np.uint64(16))
+    return u >= np.uint64(thr)

@@ -62,30 +62,38 @@ def test_philox_matches_independent_engine(aten_philox):
         assert [int(g) for g in got] == [int(x) for x in w], (seed, sub, off)
 
 
-def test_keep_mask_uses_word_j_mod_4_of_counter_j_div_4(aten_philox):
+def test_keep_mask_uses_half_j_mod_2_of_word_j_mod_8_div_2_of_counter_j_div_8(aten_philox):
     seed, rho, lane = 0x1234_5678_9ABC, 0.1, 37
-    rows, cols = np.arange(5, 9), np.arange(0, 13)
+    rows, cols = np.arange(5, 9), np.arange(0, 21)
     keep = philox.keep_mask(seed, rho, lane, rows, cols)
     thr = philox.drop_threshold(rho)
-    inp = "".join(f"{seed} {lane} {(i << 32) + j4}\n" for i in rows for j4 in range(4))
+    inp = "".join(f"{seed} {lane} {(i << 32) + j8}\n" for i in rows for j8 in range(3))
     out = subprocess.run([aten_philox], input=inp, capture_output=True, text=True, check=True).stdout
-    words = np.array([[int(w) for w in l.split()] for l in out.strip().splitlines()]).reshape(len(rows), 4, 4)
+    words = np.array([[int(w) for w in l.split()] for l in out.strip().splitlines()]).reshape(len(rows), 3, 4)
     for a, i in enumerate(rows):
         for b, j in enumerate(cols):
-            assert keep[a, b] == (words[a, j // 4, j % 4] >= thr)
+            u = (words[a, j // 8, (j % 8) // 2] >> (16 * (j % 2))) & 0xFFFF
+            assert keep[a, b] == (u >= thr)
 
 
 def test_keep_rate_is_within_five_sigma():
     rho = 0.1
     keep = philox.keep_mask(0, rho, 3, np.arange(256), np.arange(1024))
-    p = 1.0 - philox.drop_threshold(rho) / 2**32
+    p = 1.0 - philox.drop_threshold(rho) / 2**16
     n = keep.size
     assert abs(keep.mean() - p) < 5 * np.sqrt(p * (1 - p) / n)
 
 
+def test_both_halves_of_a_word_are_used_independently():
+    # a plausible slip (one half read twice) would make keys 2w and 2w+1 agree
+    keep = philox.keep_mask(7, 0.5, 1, np.arange(64), np.arange(512))
+    assert (keep[:, 0::2] != keep[:, 1::2]).mean() > 0.45
+
+
 def test_threshold_rule():
     assert philox.drop_threshold(0.0) == 0
-    assert philox.drop_threshold(0.5) == 2**31
-    assert philox.drop_threshold(float(np.float32(0.1))) == int(np.floor(float(np.float32(0.1)) * 2**32))
+    assert philox.drop_threshold(0.5) == 2**15
+    assert philox.drop_threshold(float(np.float32(0.1))) == 6553
+    assert philox.drop_threshold(0.99999) == 65535
     with pytest.raises(ValueError):
         philox.drop_threshold(1.0)
