@@ -145,19 +145,19 @@ __device__ __forceinline__ typename E::vec8 as_vec8(u32x4 u) {
 template <int ROWB> struct Swizzle;
 template <> struct Swizzle<256> {  // 128 16-bit columns
   static constexpr int MASK = 15;
-  static __device__ __forceinline__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+  static constexpr __host__ __device__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 };
 template <> struct Swizzle<128> {  // 64 16-bit columns: two rows share a bank line
   static constexpr int MASK = 7;
-  static __device__ __forceinline__ int f(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+  static constexpr __host__ __device__ int f(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 };
 template <> struct Swizzle<1152> {  // 576 16-bit columns: alternate rows start half a bank line apart
   static constexpr int MASK = 7;
-  static __device__ __forceinline__ int f(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+  static constexpr __host__ __device__ int f(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 };
 
 template <int ROWB>
-__device__ __forceinline__ int phys_chunk(int row, int chunk) {
+constexpr __host__ __device__ int phys_chunk(int row, int chunk) {
   constexpr int M = Swizzle<ROWB>::MASK;
   return (chunk & ~M) | ((chunk & M) ^ Swizzle<ROWB>::f(row));
 }
@@ -220,7 +220,11 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_
 // caller masks them), so no access leaves the tensor.  Completion is awaited
 // with a vmcnt wait before the barrier that publishes the tile.  The per-lane
 // parts of the offsets are computed once; an issue costs three VALU
-// operations per instruction (row clamp and byte offset).
+// operations per instruction (row clamp and byte offset), plus one XOR where
+// the swizzle of the instruction's rows differs from that of the first
+// instruction's by the same XOR in every lane of every wave (checked at
+// compile time): then one register per lane holds the column offsets instead
+// of one per instruction.
 template <int ROWS, int W, int NWAVES>
 struct TileCopy {
   static constexpr int CPR = W / 8;  // 16-byte chunks per row
@@ -228,20 +232,37 @@ struct TileCopy {
   static_assert(INSTS % NWAVES == 0 && 64 % CPR == 0, "tile does not split evenly over the waves");
   static constexpr int PER_WAVE = INSTS / NWAVES;
   static constexpr int RPI = 64 / CPR;  // rows per instruction
+  static constexpr int row_of(int wave, int lane) { return wave * PER_WAVE * RPI + lane / CPR; }
+  static constexpr int xor_of(int u) { return Swizzle<2 * W>::f(u * RPI) ^ Swizzle<2 * W>::f(0); }
+  static constexpr bool xor_uniform() {
+    for (int w = 0; w < NWAVES; ++w)
+      for (int l = 0; l < 64; ++l)
+        for (int u = 0; u < PER_WAVE; ++u) {
+          const int r = row_of(w, l);
+          if ((Swizzle<2 * W>::f(r + u * RPI) ^ Swizzle<2 * W>::f(r)) != xor_of(u)) return false;
+        }
+    return true;
+  }
+  static constexpr bool XOR = xor_uniform();
+  static constexpr int NCOL = XOR ? 1 : PER_WAVE;
   int row;                // tile row of this lane in the wave's first instruction
-  int col[PER_WAVE];      // byte offset, within its row, of the chunk this lane fetches
+  int col[NCOL];          // byte offset, within its row, of the chunk this lane fetches
   int inst0;              // first instruction index of the wave (uniform)
   __device__ __forceinline__ TileCopy(int wave, int lane) {
     inst0 = wave * PER_WAVE;
-    row = inst0 * RPI + lane / CPR;
+    row = row_of(wave, lane);
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) col[u] = phys_chunk<2 * W>(row + u * RPI, lane % CPR) * 16;  // involution
+    for (int u = 0; u < NCOL; ++u) col[u] = phys_chunk<2 * W>(row + u * RPI, lane % CPR) * 16;  // involution
+  }
+  __device__ __forceinline__ int col_of(int u) const {
+    if constexpr (XOR) return col[0] ^ (xor_of(u) * 16);
+    else return col[u];
   }
   // instruction u (0 .. PER_WAVE-1) of the wave's share; rs covers the tensor
   // whose row 0 is at offset 0
   __device__ __forceinline__ void issue_one(char ETS_LDS* dst, __amdgpu_buffer_rsrc_t rs, int row0, int last_row,
                                             int u) const {
-    const unsigned off = (unsigned)min(row0 + row + u * RPI, last_row) * (unsigned)(2 * W) + (unsigned)col[u];
+    const unsigned off = (unsigned)min(row0 + row + u * RPI, last_row) * (unsigned)(2 * W) + (unsigned)col_of(u);
     copy16_to_lds(rs, off, (void ETS_LDS*)(dst + (inst0 + u) * 1024));
   }
   __device__ __forceinline__ void issue(char ETS_LDS* dst, __amdgpu_buffer_rsrc_t rs, int row0, int last_row) const {
