@@ -13,7 +13,7 @@
 // are summed into the shared head.
 //
 // Three kernels, all on the caller's stream:
-//   prep  D_i from G and Y (fp32, into the workspace);
+//   prep  -D_i from G and Y (fp32, into the workspace);
 //   dkdv  key-major: a workgroup owns 128 keys of one K/V head, keeps its K
 //         and V rows in registers as MFMA B operands, and walks every query
 //         tile (and every query head of the group) that can see them; S = Q K^T
@@ -28,9 +28,10 @@
 namespace ets {
 
 // --------------------------------------------------------------------- prep
-// D_i = G_i . Y_i and the base-2 LSE, LSE_i log2(e) (+inf for a row with an
-// empty allowed set, so every recomputed weight of it is 0).  The 64 rows after
-// the last are filled with D = 0, LSE2 = +inf: tiles of 64 rows may read them.
+// -D_i = -(G_i . Y_i) and the base-2 LSE, LSE_i log2(e) (+inf for a row with
+// an empty allowed set, so every recomputed weight of it is 0).  The 64 rows
+// after the last are filled with D = 0, LSE2 = +inf: tiles of 64 rows may read
+// them.  -D is stored so that it can start a dP accumulator (dP - D).
 template <class E, int D>
 __global__ __launch_bounds__(256) void dense_bwd_prep_kernel(const DenseArgs a, int rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void dense_bwd_prep_kernel(const DenseArgs a, 
     } else {
       acc = 0.f;
     }
-    a.Dws[row] = acc;
+    a.Dws[row] = -acc;
     a.Lws[row] = l2;
   }
 }
@@ -83,6 +84,16 @@ __device__ __forceinline__ void keep8_rows(const DropArgs& d, int lane_bh, int i
 }
 
 // --------------------------------------------------------------------- dK, dV
+// Order of the 2 KS products of an A group (S = K Q^T and dP = V G^T of one
+// 32-row block, KS k-steps each): S(0), S(1), then dP(k) and S(k + 2)
+// alternating, dP(KS - 1) last, so the first dP product comes two slots after
+// the group starts (its accumulator starts from -D, read from LDS there).
+template <int KS>
+constexpr bool a_is_dp(int u) { return u >= 2 && ((u & 1) == 0 || u == 2 * KS - 1); }
+template <int KS>
+constexpr int a_kstep(int u) {
+  return a_is_dp<KS>(u) ? (u == 2 * KS - 1 ? KS - 1 : (u - 2) / 2) : (u < 2 ? u : (u + 1) / 2);
+}
 // Group plans of a step with NMQ query blocks: group gi is A (S, dP) or B
 // (dV, dK) of block mq[gi]; W(wq[gi]) runs under group gi, the LSE / D rows
 // of W(nwq[gi]) are read at its end, and the copies of the next step are
@@ -271,10 +282,8 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     auto operand = [&](auto stg, int t) __attribute__((always_inline)) {
       const int gi = plan_group<Plan>(t, NA, NB);
       const int u = t - plan_start<Plan>(gi, NA, NB), mq = Plan::mq[gi];
-      if (Plan::isA[gi]) {
-        const int kk = u / 2;
-        return as_vec8<E>(lds_b128((u & 1) ? gbuf(stg) : qbuf(stg), rops.off(32 * mq, kk)));
-      }
+      if (Plan::isA[gi])
+        return as_vec8<E>(lds_b128(a_is_dp<KS>(u) ? gbuf(stg) : qbuf(stg), rops.off(32 * mq, a_kstep<KS>(u))));
       const int kh = u / (2 * MD), md = (u % (2 * MD)) / 2;
       return as_vec8<E>(tops.read((u & 1) ? qbuf(stg) : gbuf(stg), 32 * mq + 16 * kh, md));
     };
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qr = 32 * mq + 8 * g4 + 4 * h32;
         w.l4[g4] = *(const f32x4 ETS_LDS*)(ls + qr);
-        w.d4[g4] = *(const f32x4 ETS_LDS*)(ls + 128 + qr);  // D after 128 LSE2 floats
+        if constexpr (DROP) w.d4[g4] = *(const f32x4 ETS_LDS*)(ls + 128 + qr);  // -D after 128 LSE2 floats
       }
     };
     // sub-part k = 2 g4 + half: rows r2 = 2 half, 2 half + 1 of group g4
@@ -341,7 +350,9 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         }
         const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
         pk[e] = (al && kp) ? pv : 0.f;
-        gm[e] = al ? pv * (dpv - w.d4[g4][r2]) : 0.f;
+        // without dropout the dP accumulator started from -D
+        if constexpr (DROP) dpv += w.d4[g4][r2];
+        gm[e] = al ? pv * dpv : 0.f;
       }
       w.pw[2 * g4 + half] = E::pack2(pk[0], pk[1]);
       w.gw[2 * g4 + half] = E::pack2(gm[0], gm[1]);
@@ -375,12 +386,24 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         if constexpr (t + 3 < NSLOT) opb[(t + 3) % 4] = operand(stg, t + 3);
         const vec8 op = opb[t % 4];
         if constexpr (isA) {
-          constexpr int kk = u / 2;
+          constexpr int kk = a_kstep<KS>(u);
           if constexpr (u == 0) {
 #pragma unroll
-            for (int r2 = 0; r2 < 16; ++r2) { sc[mq][r2] = 0.f; dp[mq][r2] = 0.f; }
+            for (int r2 = 0; r2 < 16; ++r2) sc[mq][r2] = 0.f;
+            if constexpr (DROP) {
+#pragma unroll
+              for (int r2 = 0; r2 < 16; ++r2) dp[mq][r2] = 0.f;
+            } else {  // dP starts from -D of its rows (the first dP product is two slots on)
+              const float ETS_LDS* ls = (const float ETS_LDS*)lbuf(stg);
+#pragma unroll
+              for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x = *(const f32x4 ETS_LDS*)(ls + 128 + 32 * mq + 8 * g4 + 4 * h32);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dp[mq][4 * g4 + r] = x[r];
+              }
+            }
           }
-          if constexpr (u & 1) dp[mq] = E::mfma32(op, vreg[kk], dp[mq]);
+          if constexpr (a_is_dp<KS>(u)) dp[mq] = E::mfma32(op, vreg[kk], dp[mq]);
           else sc[mq] = E::mfma32(op, kreg[kk], sc[mq]);
         } else {
           constexpr int kh = u / (2 * MD), md = (u % (2 * MD)) / 2;
@@ -584,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       greg[kk] = as_vec8<E>(gv);
     }
     const float lse2 = (qi < nq) ? a.Lws[(size_t)bh * nq + qi] : __builtin_huge_valf();
-    const float dval = (qi < nq) ? a.Dws[(size_t)bh * nq + qi] : 0.f;
+    const float ndval = (qi < nq) ? a.Dws[(size_t)bh * nq + qi] : 0.f;  // -D
     f32x16 dq[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md)
@@ -662,7 +685,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
         float dpv = dp[4 * g4 + r2];
         if constexpr (DROP) dpv = ((w.keep >> (8 * g4 + r2)) & 1u) ? dpv * a.drop.inv_keep : 0.f;
         const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
-        gm[e] = al ? pv * (dpv - dval) : 0.f;
+        gm[e] = al ? pv * (dpv + ndval) : 0.f;
       }
       w.gw[2 * g4 + half] = E::pack2(gm[0], gm[1]);
       materialize(w.gw[2 * g4 + half]);
