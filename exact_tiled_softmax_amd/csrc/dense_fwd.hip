@@ -71,8 +71,35 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
   // (boustrophedon over the heaviest-first list), which balances the causal
   // triangle without atomics and keeps every slot busy until the end.
   const int G = (int)gridDim.x, n_items = n_qtiles * a.B * a.H;
+  auto item_of = [&](int r) { return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  // key-tile range of query tile qt
+  auto tile_range = [&](int qt, int& lo, int& hi) __attribute__((always_inline)) {
+    const int q0 = qt * BQ, qlast = min(q0 + BQ, a.nq) - 1;
+    lo = 0;
+    hi = (a.nk - 1) / BK;
+    if (a.mask.causal) hi = min(hi, qlast / BK);
+    if (a.mask.window > 0) lo = max(0, (q0 - a.mask.window + 1) / BK);
+  };
+  // The wave priority follows the key tiles the workgroup has left, so of two
+  // workgroups sharing a compute unit the one further behind issues first
+  // (with equal priorities the older one wins every tie, and the younger one
+  // ends alone on the unit).  rem is uniform: a scalar.
+  int rem = 0;
   for (int r = 0; r * G < n_items; ++r) {
-    const int item = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    const int item = item_of(r);
+    if (item >= n_items) continue;
+    int lo, hi;
+    tile_range(n_qtiles - 1 - item / (a.B * a.H), lo, hi);
+    rem += max(hi - lo + 1, 0);
+  }
+  auto set_prio = [&]() __attribute__((always_inline)) {
+    if (rem > 16) __builtin_amdgcn_s_setprio(3);
+    else if (rem > 8) __builtin_amdgcn_s_setprio(2);
+    else if (rem > 3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = item_of(r);
     if (item >= n_items) continue;
     // work item = one query tile of one (batch, head); items are numbered
     // heaviest first and consecutive items walk (batch, head)
@@ -108,10 +135,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     float mref = kNegInf, lsum = 0.f;
 
     // key-tile range of the workgroup
-    const int qlast = min(q0 + BQ, nq) - 1;
-    int jt_lo = 0, jt_hi = (nk - 1) / BK;
-    if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
-    if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
+    int jt_lo, jt_hi;
+    tile_range(qt, jt_lo, jt_hi);
 
     const TileCopy<BK, D, NW> tcopy(wave, lane);
     constexpr int NCOPY = 2 * TileCopy<BK, D, NW>::PER_WAVE;  // copy instructions per wave per tile
@@ -359,6 +384,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       __syncthreads();
     };
     auto general_step = [&](auto st, int jt, int jn) __attribute__((always_inline)) {
+      set_prio();
+      --rem;
       const int j0 = jt * BK;
       const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nq, nk);
       const int cls = cinfo & kClassMask;
@@ -381,6 +408,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       // a fixed-order range exists (arithmetic masks only): general_run stopped
       // at tile number fp0 < N, so jt = jt_lo + p here and tile p + 1 is full too
       for (; p < fp1; p += 2) {
+        set_prio();
+        rem -= 2;
         tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
         finish();
         const int jn = next_of(jt + 1);
