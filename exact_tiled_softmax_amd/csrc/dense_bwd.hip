@@ -579,8 +579,34 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
   // Persistent workgroups over (query tile, (batch, head)), heaviest query
   // tiles first, in boustrophedon order.
   const int G = (int)gridDim.x, n_items = n_qtiles * BH;
+  auto item_of = [&](int r) { return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  // key-tile range of query tile qt
+  auto tile_range = [&](int qt, int& lo, int& hi) __attribute__((always_inline)) {
+    const int q0 = qt * BQ, qlast = min(q0 + BQ, nq) - 1;
+    lo = 0;
+    hi = (nk - 1) / BK;
+    if (a.mask.causal) hi = min(hi, qlast / BK);
+    if (a.mask.window > 0) lo = max(0, (q0 - a.mask.window + 1) / BK);
+  };
+  // The wave priority follows the key tiles the workgroup has left, so of two
+  // workgroups sharing a compute unit the one further behind issues first
+  // (with equal priorities the older one wins every tie).  rem is a scalar.
+  int rem = 0;
   for (int r = 0; r * G < n_items; ++r) {
-    const int item = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    const int item = item_of(r);
+    if (item >= n_items) continue;
+    int lo, hi;
+    tile_range(n_qtiles - 1 - item / BH, lo, hi);
+    rem += max(hi - lo + 1, 0);
+  }
+  auto set_prio = [&]() __attribute__((always_inline)) {
+    if (rem > 16) __builtin_amdgcn_s_setprio(3);
+    else if (rem > 8) __builtin_amdgcn_s_setprio(2);
+    else if (rem > 3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = item_of(r);
     if (item >= n_items) continue;
     const int qt = n_qtiles - 1 - item / BH;
     const int bh = item % BH;
@@ -614,10 +640,8 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
 #pragma unroll
       for (int r2 = 0; r2 < 16; ++r2) dq[md][r2] = 0.f;
 
-    const int qlast = min(q0 + BQ, nq) - 1;
-    int jt_lo = 0, jt_hi = (nk - 1) / BK;
-    if (a.mask.causal) jt_hi = min(jt_hi, qlast / BK);
-    if (a.mask.window > 0) jt_lo = max(0, (q0 - a.mask.window + 1) / BK);
+    int jt_lo, jt_hi;
+    tile_range(qt, jt_lo, jt_hi);
     auto wg_nonempty = [&](int jt) {
       return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
     };
@@ -758,6 +782,8 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       __syncthreads();
     };
     auto general_step = [&](auto st, int jt, int jn) __attribute__((always_inline)) {
+      set_prio();
+      --rem;
       const int j0 = jt * BK;
       const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nq, nk);
       const int cls = cinfo & kClassMask;
@@ -808,6 +834,8 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       // general_run stopped at tile number fp0 < N: jt = jt_lo + p, and
       // tile p + 1 is whole too
       for (; p < fp1; p += 2) {
+        set_prio();
+        rem -= 2;
         tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
         finish();
         const int jn = next_of(jt + 1);
