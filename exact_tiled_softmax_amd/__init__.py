@@ -16,13 +16,15 @@ import os
 
 __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
-    "ATTN_F32", "ATTN_F16", "ATTN_BF16", "AttnError", "Mask", "Dropout",
+    "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
     "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
+    "attn_sparse_fwd_lse", "attn_sparse_bwd_lse",
     "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_status_string", "library_path", "lib",
 ]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_F16, ATTN_BF16 = range(3)
+ATTN_LSE_TOTAL, ATTN_LSE_KV = range(2)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn.so")
@@ -90,6 +92,10 @@ lib.attn_sparse_bwd_workspace_size.restype = _sz
 lib.attn_sparse_bwd_workspace_size.argtypes = [_i] * 6
 lib.attn_sparse_bwd.restype = _i
 lib.attn_sparse_bwd.argtypes = ([_i] + [_i] * 6 + [_vp] * 5 + [_f] + [_vp] * 3 + [_vp] * 3 + [_vp, _sz, _vp])
+lib.attn_sparse_fwd_lse.restype = _i
+lib.attn_sparse_fwd_lse.argtypes = [_i] + lib.attn_sparse_fwd.argtypes
+lib.attn_sparse_bwd_lse.restype = _i
+lib.attn_sparse_bwd_lse.argtypes = [_i] + lib.attn_sparse_bwd.argtypes
 lib.attn_dropout_mask.restype = _i
 lib.attn_dropout_mask.argtypes = [_f, ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
 lib.attn_mfma_probe.restype = _i
@@ -187,6 +193,14 @@ def attn_sparse_fwd(dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_lengt
     return _check(st, "attn_sparse_fwd", raise_on_error)
 
 
+def attn_sparse_fwd_lse(kind, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                        O, LSE, stream=None, raise_on_error=True):
+    st = lib.attn_sparse_fwd_lse(int(kind), dt, Tq, H, Tkv, d_qk, d_v, topk, _ptr(Q), _ptr(KV), _ptr(topk_idx),
+                                 _ptr(topk_length), _ptr(attn_sink), float(scale), _ptr(O), _ptr(LSE),
+                                 _stream(stream))
+    return _check(st, "attn_sparse_fwd_lse", raise_on_error)
+
+
 def attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk):
     return lib.attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk)
 
@@ -199,6 +213,16 @@ def attn_sparse_bwd(dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_lengt
                              _ptr(dO), _ptr(dQ), _ptr(dKV), _ptr(dSink), _ptr(workspace),
                              int(workspace_bytes), _stream(stream))
     return _check(st, "attn_sparse_bwd", raise_on_error)
+
+
+def attn_sparse_bwd_lse(kind, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                        O, LSE, dO, dQ, dKV, dSink, workspace, workspace_bytes, stream=None,
+                        raise_on_error=True):
+    st = lib.attn_sparse_bwd_lse(int(kind), dt, Tq, H, Tkv, d_qk, d_v, topk, _ptr(Q), _ptr(KV), _ptr(topk_idx),
+                                 _ptr(topk_length), _ptr(attn_sink), float(scale), _ptr(O), _ptr(LSE),
+                                 _ptr(dO), _ptr(dQ), _ptr(dKV), _ptr(dSink), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
+    return _check(st, "attn_sparse_bwd_lse", raise_on_error)
 
 
 def attn_dropout_mask(rate, seed, B, H, n_q, n_k, xi, stream=None, raise_on_error=True):

@@ -187,10 +187,11 @@ static void fill_sparse(SparseArgs& a, int Tq, int H, int Tkv, int d_qk, int d_v
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
 }
 
-attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
-                            const void* Q, const void* KV, const int32_t* topk_idx,
-                            const int32_t* topk_length, const float* attn_sink, float scale,
-                            void* O, float* LSE, void* stream) {
+attn_status attn_sparse_fwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale, void* O,
+                                float* LSE, void* stream) {
+  if (kind != ATTN_LSE_TOTAL && kind != ATTN_LSE_KV) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_sparse(dt, Tq, H, Tkv, d_qk, d_v, topk, scale);
   if (st != ATTN_OK) return st;
   if (!Q || !KV || !topk_idx || !O || !LSE) return ATTN_ERR_INVALID_ARG;
@@ -203,8 +204,17 @@ attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
   fill_sparse(a, Tq, H, Tkv, d_qk, d_v, topk, scale);
   a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
   a.O = O; a.LSE = LSE;
+  a.lse_kv = kind == ATTN_LSE_KV;
   const int rc = launch_sparse_fwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                            const void* Q, const void* KV, const int32_t* topk_idx,
+                            const int32_t* topk_length, const float* attn_sink, float scale,
+                            void* O, float* LSE, void* stream) {
+  return attn_sparse_fwd_lse(ATTN_LSE_TOTAL, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length,
+                             attn_sink, scale, O, LSE, stream);
 }
 
 size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk) {
@@ -213,11 +223,12 @@ size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v,
   return 2 * round_up((size_t)Tq * H * sizeof(float)) + round_up((size_t)Tkv * d_qk * sizeof(float));
 }
 
-attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
-                            const void* Q, const void* KV, const int32_t* topk_idx,
-                            const int32_t* topk_length, const float* attn_sink, float scale,
-                            const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
-                            float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
+attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale,
+                                const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                                float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
+  if (kind != ATTN_LSE_TOTAL && kind != ATTN_LSE_KV) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_sparse(dt, Tq, H, Tkv, d_qk, d_v, topk, scale);
   if (st != ATTN_OK) return st;
   if (!Q || !KV || !topk_idx || !O || !LSE || !dO || !dQ || !dKV) return ATTN_ERR_INVALID_ARG;
@@ -233,11 +244,21 @@ attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
   fill_sparse(a, Tq, H, Tkv, d_qk, d_v, topk, scale);
   a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
   a.O = (void*)O; a.LSE = (float*)LSE; a.dO = dO; a.dQ = dQ; a.dKV = dKV; a.dSink = dSink;
+  a.lse_kv = kind == ATTN_LSE_KV;
   a.Dws = (float*)workspace;
   a.dsink_part = (float*)((char*)workspace + round_up((size_t)Tq * H * sizeof(float)));
   a.dKVws = (float*)((char*)workspace + 2 * round_up((size_t)Tq * H * sizeof(float)));
   const int rc = launch_sparse_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
+                            const void* Q, const void* KV, const int32_t* topk_idx,
+                            const int32_t* topk_length, const float* attn_sink, float scale,
+                            const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                            float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_sparse_bwd_lse(ATTN_LSE_TOTAL, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length,
+                             attn_sink, scale, O, LSE, dO, dQ, dKV, dSink, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_dropout_mask(float rate, uint64_t seed, int B, int H, int n_q, int n_k,

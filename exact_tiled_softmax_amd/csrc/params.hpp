@@ -54,6 +54,7 @@ struct SparseArgs {
   float* dKVws;      // [Tkv*dqk] fp32 accumulation
   int Tq, H, Tkv, dqk, dv, topk;
   float scale, scale_log2;
+  int lse_kv;        // 1: the LSE written / read covers the selected KV logits only (no sink)
 };
 
 // Kernel launchers (defined in the .hip files).  Each returns 0 on success or

@@ -207,6 +207,8 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
     scale_o = (lt > 0.f) ? fo / lt : 0.f;
     lse = (M + __log2f(lt)) * kLn2;
   }
+  // KV-only convention: ln sum_u e^{s_u}, the sink left out (-inf without rows)
+  if (a.lse_kv) lse = (mref == kNegInf || !(l > 0.f)) ? kNegInf : (mref + __log2f(l)) * kLn2;
   uint16_t* Oh = (uint16_t*)a.O + ((size_t)t * H + head) * DV;
 #pragma unroll
   for (int m = 0; m < MV; ++m) {
@@ -219,6 +221,17 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
 }
 
 // ------------------------------------------------------------------ backward
+// The sink-inclusive LSE of (token, head) from the saved one: a KV-only LSE is
+// first combined with the sink logit, LSE_total = logaddexp(LSE_kv, z)
+// ([P5] section 7.2); every reconstructed probability uses LSE_total.
+__device__ __forceinline__ float lse_total(const SparseArgs& a, size_t th, int head) {
+  const float lse = a.LSE[th];
+  if (!a.lse_kv || !a.sink) return lse;
+  const float z = a.sink[head];
+  const float hi = fmaxf(lse, z), lo = fminf(lse, z);
+  return (lo == kNegInf) ? hi : hi + log1pf(expf(lo - hi));
+}
+
 // D[t][h] = dO . O ; zero the fp32 dKV accumulator
 template <class E>
 __global__ __launch_bounds__(256) void sparse_bwd_prep_kernel(const SparseArgs a) {
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
   for (int kk = 0; kk < KSQ; ++kk) qreg[kk] = as_vec8<E>(*(const u32x4*)(Qh + 32 * kk + 8 * G));
 #pragma unroll
   for (int kk = 0; kk < KSV; ++kk) greg[kk] = as_vec8<E>(*(const u32x4*)(Gh + 32 * kk + 8 * G));
-  const float lse = a.LSE[th];
+  const float lse = lse_total(a, th, head);
   const float lse2 = (lse == kNegInf) ? 0.f : lse * kLog2e;
   const float Dv = a.Dws[th];
 
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
 #pragma unroll
     for (int kk = 0; kk < KSV; ++kk) greg[kk] = as_vec8<E>(*(const u32x4*)(Gh + 32 * kk + 8 * G));
   }
-  const float lse = a.LSE[th];
+  const float lse = lse_total(a, th, head);
   const float lse2 = (lse == kNegInf) ? 0.f : lse * kLog2e;
   const float Dv = a.Dws[th];
 

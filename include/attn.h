@@ -188,6 +188,25 @@ attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
                             const int32_t* topk_length, const float* attn_sink, float scale,
                             void* O, float* LSE, void* stream);
 
+/*
+ * LSE conventions of the sparse path ([P5] sections 7.1-7.2).  ATTN_LSE_TOTAL:
+ * ln(e^{z_h} + sum_u e^{s_u}), the sink included (attn_sparse_fwd's export).
+ * ATTN_LSE_KV: ln sum_u e^{s_u} over the selected KV logits only (-inf for a
+ * token with no selected row), as some sparse forward contracts return it; a
+ * backward pass given it first forms LSE_total = logaddexp(LSE_kv, z_h) and
+ * reconstructs every probability from that.
+ */
+typedef enum { ATTN_LSE_TOTAL = 0, ATTN_LSE_KV = 1 } attn_lse_kind;
+
+/*
+ * attn_sparse_fwd_lse -- attn_sparse_fwd with the LSE exported in convention
+ * `kind` (O is the same either way).  INVALID_ARG for any other kind.
+ */
+attn_status attn_sparse_fwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale, void* O,
+                                float* LSE, void* stream);
+
 /* Bytes of device workspace attn_sparse_bwd needs (fp32 D and sink-gradient
  * terms per (token, head), and an fp32 [Tkv][d_qk] dKV accumulator). */
 size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk);
@@ -210,6 +229,18 @@ attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int
                             const int32_t* topk_length, const float* attn_sink, float scale,
                             const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
                             float* dSink, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_sparse_bwd_lse -- attn_sparse_bwd for an LSE saved in convention
+ * `kind` (see attn_lse_kind); with ATTN_LSE_KV and a sink, LSE_total =
+ * logaddexp(LSE_kv, z_h) is formed per (token, head) before any probability
+ * is reconstructed ([P5] section 7.2).  INVALID_ARG for any other kind.
+ */
+attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale,
+                                const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                                float* dSink, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_dropout_mask -- writes the dropout realisation xi that attn_fwd and

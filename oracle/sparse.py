@@ -16,6 +16,8 @@ Follows icavan.github.io, "DeepSeek Sparse Attention Forward and Backward":
               dKV[I_u, Dv:] += dK, reduced over every token and head;
               dz = -p_sink D summed over tokens per head.
   section 7.1 the saved LSE is the sink-inclusive ln Z (natural log).
+  section 7.2 a KV-only LSE, ln sum_u e^{s_u}, leaves the sink out; a
+              backward pass given it forms LSE_total = logaddexp(LSE_kv, z).
 
 Slots u >= topk_length[t] are padding and are never read.  A token with no
 valid slot and no sink has an empty row: O = 0 and LSE = -inf; with a sink it
@@ -55,6 +57,30 @@ def forward(Q, KV, idx, length, sink, alpha, dv, tokens=None):
         O[t] = p @ Ks[:, :dv]
         LSE[t] = lse
     return O, LSE
+
+
+def lse_kv(Q, KV, idx, length, alpha, tokens=None):
+    """KV-only LSE [Tq, H] (section 7.2): ln sum_u e^{s_u} over the selected
+    rows, written out directly (-inf for a token with no selected row)."""
+    Tq, H, _ = Q.shape
+    out = np.zeros((Tq, H))
+    for t in (range(Tq) if tokens is None else tokens):
+        L = idx.shape[1] if length is None else int(length[t])
+        if L == 0:
+            out[t] = -np.inf
+            continue
+        Ks = np.asarray(KV[np.asarray(idx[t, :L], dtype=np.int64)], dtype=np.float64)
+        s = alpha * (np.asarray(Q[t], dtype=np.float64) @ Ks.T)   # [H, L]
+        top = s.max(axis=1)
+        out[t] = top + np.log(np.exp(s - top[:, None]).sum(axis=1))
+    return out
+
+
+def lse_total_from_kv(lse_kv_, sink):
+    """Section 7.2's normalisation: LSE_total = logaddexp(LSE_kv, z)."""
+    if sink is None:
+        return np.asarray(lse_kv_, dtype=np.float64)
+    return np.logaddexp(lse_kv_, np.asarray(sink, dtype=np.float64)[None, :])
 
 
 def vjp(Q, KV, idx, length, sink, alpha, dv, dO, tokens=None):

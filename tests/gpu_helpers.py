@@ -96,8 +96,9 @@ def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=
     return res
 
 
-def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None):
-    """Run attn_sparse_fwd (and attn_sparse_bwd when dO is given)."""
+def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None, lse_kind=None):
+    """Run attn_sparse_fwd (and attn_sparse_bwd when dO is given); with
+    lse_kind, the _lse entry points in that LSE convention."""
     import exact_tiled_softmax_amd as ets
     torch = torch_cuda()
     Tq, H, dqk = Q.shape
@@ -111,7 +112,10 @@ def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None):
     ds = None if sink is None else torch.from_numpy(np.ascontiguousarray(sink, np.float32)).cuda()
     O = empty((Tq, H, dv), dtype)
     LSE = torch.zeros((Tq, H), dtype=torch.float32, device="cuda")
-    ets.attn_sparse_fwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE)
+    if lse_kind is None:
+        ets.attn_sparse_fwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE)
+    else:
+        ets.attn_sparse_fwd_lse(lse_kind, dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE)
     out = {"O": O, "LSE": LSE}
     if dO is not None:
         g = to_dev(dO, dtype)
@@ -119,8 +123,12 @@ def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None):
         dSink = torch.zeros(H, dtype=torch.float32, device="cuda") if sink is not None else None
         nb = ets.attn_sparse_bwd_workspace_size(Tq, H, Tkv, dqk, dv, topk)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        ets.attn_sparse_bwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE, g, dQ, dKV, dSink,
-                            ws, nb)
+        if lse_kind is None:
+            ets.attn_sparse_bwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE, g, dQ, dKV, dSink,
+                                ws, nb)
+        else:
+            ets.attn_sparse_bwd_lse(lse_kind, dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE, g,
+                                    dQ, dKV, dSink, ws, nb)
         out.update(dQ=dQ, dKV=dKV)
         if dSink is not None:
             out["dSink"] = dSink

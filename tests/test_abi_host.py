@@ -106,6 +106,19 @@ def test_sparse_bwd_needs_dsink_with_sink_and_a_workspace():
     assert st == ets.ATTN_ERR_WORKSPACE
 
 
+def test_sparse_lse_kind_is_checked_before_launch():
+    import exact_tiled_softmax_amd as ets
+    assert ets.attn_sparse_fwd_lse(2, ets.ATTN_BF16, 8, 64, 32, 576, 512, 16, P, P, P, None, None, 0.04, P, P,
+                                   stream=0, raise_on_error=False) == ets.ATTN_ERR_INVALID_ARG
+    need = ets.attn_sparse_bwd_workspace_size(8, 64, 32, 576, 512, 16)
+    assert ets.attn_sparse_bwd_lse(-1, ets.ATTN_BF16, 8, 64, 32, 576, 512, 16, P, P, P, None, None, 0.04, P, P, P,
+                                   P, P, None, P, need, stream=0, raise_on_error=False) == ets.ATTN_ERR_INVALID_ARG
+    # a valid kind still goes through the same checks (missing workspace)
+    assert ets.attn_sparse_bwd_lse(ets.ATTN_LSE_KV, ets.ATTN_BF16, 8, 64, 32, 576, 512, 16, P, P, P, None, None,
+                                   0.04, P, P, P, P, P, None, None, need, stream=0,
+                                   raise_on_error=False) == ets.ATTN_ERR_WORKSPACE
+
+
 def test_dropout_mask_rejects_bad_rate():
     import exact_tiled_softmax_amd as ets
     assert ets.attn_dropout_mask(1.0, 0, 1, 1, 4, 4, P, stream=0, raise_on_error=False) == ets.ATTN_ERR_INVALID_ARG

@@ -100,3 +100,30 @@ def test_sparse_page_example_embedded():
     np.testing.assert_allclose(r["dKV"][:, 0], H * np.asarray(pr["p"]) * pr["g"], rtol=2e-3)
     np.testing.assert_allclose(r["dKV"][:, 575], H * np.asarray(pr["dS"]), rtol=5e-3)
     np.testing.assert_allclose(r["dSink"], pr["dz"], atol=2e-3)
+
+
+@pytest.mark.parametrize("sink", [True, False])
+def test_sparse_kv_only_lse_export_and_backward(sink):
+    # [P5] section 7.2: the KV-only LSE leaves the sink out; the backward given
+    # it normalises with logaddexp(LSE_kv, z) and must reach the same gradients
+    import exact_tiled_softmax_amd as ets
+    c = _case(20, 260, 90, "bf16", 5, sink=sink)
+    alpha = 1.0 / 24.0
+    sink64 = None if c["sink"] is None else c["sink"].astype(np.float64)
+    ref = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=c["dO"])
+    r = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=c["dO"],
+                      lse_kind=ets.ATTN_LSE_KV)
+    assert np.array_equal(r["O"], ref["O"])  # the output does not depend on the convention
+    want = sparse.lse_kv(c["Q64"], c["KV64"], c["idx"], c["L"], alpha)
+    assert gh.lse_err(r["LSE"], want) <= LSE_TOL
+    assert np.all(np.isneginf(r["LSE"][0]))  # token 0 selects no row
+    dQ, dKV, dSink = sparse.vjp(c["Q64"], c["KV64"], c["idx"], c["L"], sink64, alpha, DV, c["dO64"])
+    assert gh.rel_fro(r["dQ"], dQ) <= REL_TOL
+    assert gh.rel_fro(r["dKV"], dKV) <= REL_TOL
+    assert gh.rel_fro(r["dQ"], ref["dQ"]) <= 1e-3
+    if sink:
+        assert gh.rel_fro(r["dSink"], dSink) <= REL_TOL
+    else:
+        assert np.array_equal(r["LSE"], ref["LSE"])  # without a sink the conventions coincide
+        assert np.array_equal(r["dQ"], ref["dQ"])
+

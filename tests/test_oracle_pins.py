@@ -387,6 +387,38 @@ def test_sparse_sink_probability_and_empty_rows():
     assert np.all(O2[1] == 0) and np.all(LSE2[1] == -np.inf)
 
 
+def test_sparse_kv_only_lse_closed_form():
+    # icavan.github.io, DSA page, section 7.2: scores (0, ln 3) give LSE_kv = ln 4;
+    # a sink logit z = ln 4 makes LSE_total = logaddexp(ln 4, ln 4) = ln 8
+    Q = np.ones((1, 1, 1))
+    KV = np.array([[0.0], [np.log(3.0)]])
+    idx = np.array([[0, 1]], dtype=np.int32)
+    kv = sparse.lse_kv(Q, KV, idx, None, 1.0)
+    np.testing.assert_allclose(kv, [[np.log(4.0)]], rtol=1e-15)
+    tot = sparse.lse_total_from_kv(kv, np.array([np.log(4.0)]))
+    np.testing.assert_allclose(tot, [[np.log(8.0)]], rtol=1e-15)
+    _, LSE = sparse.forward(Q, KV, idx, None, np.array([np.log(4.0)]), 1.0, 1)
+    np.testing.assert_allclose(LSE, tot, rtol=1e-15)
+
+
+def test_sparse_kv_only_lse_normalises_to_the_sink_inclusive_lse():
+    # the two conventions computed on separate paths: the forward sums e^z into
+    # Z directly, lse_kv leaves it out and logaddexp adds it back
+    rng = np.random.default_rng(32)
+    Q, KV = rng.standard_normal((5, 3, 4)), rng.standard_normal((9, 4))
+    idx = rng.integers(0, 9, (5, 6)).astype(np.int32)
+    length = np.array([6, 0, 3, 1, 6], dtype=np.int32)
+    sink = rng.standard_normal(3)
+    kv = sparse.lse_kv(Q, KV, idx, length, 0.7)
+    assert np.all(kv[1] == -np.inf)
+    _, LSE = sparse.forward(Q, KV, idx, length, sink, 0.7, 2)
+    np.testing.assert_allclose(sparse.lse_total_from_kv(kv, sink), LSE, rtol=1e-13)
+    _, LSE0 = sparse.forward(Q, KV, idx, length, None, 0.7, 2)  # no sink: the two agree
+    np.testing.assert_array_equal(sparse.lse_total_from_kv(kv, None), kv)
+    np.testing.assert_allclose(kv[[0, 2, 3, 4]], LSE0[[0, 2, 3, 4]], rtol=1e-13)
+    assert np.all(LSE0[1] == -np.inf)
+
+
 # ------------------------------------------------------------- input rounding
 
 
