@@ -49,18 +49,25 @@ constexpr float kRescaleSlack = 8.0f;
 
 bool sparse_supported(int H, int dqk, int dv) { return H == sp::H && dqk == sp::DQK && dv == sp::DV; }
 
-// Gather of one tile of selected rows (global -> registers -> LDS).
+// Gather of one tile of selected rows (global -> registers -> LDS).  The row
+// indices of a tile are read one tile before its rows (load_idx, then fetch a
+// tile later), so a fetch never waits on an index load.
 struct Gather {
   u32x4 pre[sp::NCH];
-  __device__ __forceinline__ void fetch(const uint16_t* KV, const int32_t* idx_t, int L, int u0, int tid) {
+  int jrow[sp::NCH];  // KV row of each chunk of the next tile to fetch (-1: padding slot)
+  __device__ __forceinline__ void load_idx(const int32_t* idx_t, int L, int u0, int tid) {
 #pragma unroll
     for (int v = 0; v < sp::NCH; ++v) {
-      const int c = tid + 256 * v, row = c / sp::CPR, cc = c % sp::CPR, slot = u0 + row;
+      const int slot = u0 + (tid + 256 * v) / sp::CPR;
+      jrow[v] = slot < L ? idx_t[slot] : -1;
+    }
+  }
+  __device__ __forceinline__ void fetch(const uint16_t* KV, int tid) {
+#pragma unroll
+    for (int v = 0; v < sp::NCH; ++v) {
+      const int cc = (tid + 256 * v) % sp::CPR;
       pre[v] = u32x4{0, 0, 0, 0};
-      if (slot < L) {
-        const int j = idx_t[slot];
-        pre[v] = *(const u32x4*)(KV + (size_t)j * sp::DQK + 8 * cc);
-      }
+      if (jrow[v] >= 0) pre[v] = *(const u32x4*)(KV + (size_t)jrow[v] * sp::DQK + 8 * cc);
     }
   }
   __device__ __forceinline__ void stash(char ETS_LDS* buf, int tid) {
@@ -68,6 +75,22 @@ struct Gather {
     for (int v = 0; v < sp::NCH; ++v) {
       const int c = tid + 256 * v, row = c / sp::CPR, cc = c % sp::CPR;
       lds_st128(buf, toff<sp::ROWB>(row, 8 * cc), pre[v]);
+    }
+  }
+  // prologue: tile 0 into buf, the indices of tile 1 loaded
+  __device__ __forceinline__ void start(const uint16_t* KV, const int32_t* idx_t, int L, int ntiles,
+                                        char ETS_LDS* buf, int tid) {
+    load_idx(idx_t, L, 0, tid);
+    fetch(KV, tid);
+    stash(buf, tid);
+    if (ntiles > 1) load_idx(idx_t, L, sp::BK, tid);
+  }
+  // at the start of tile it: rows of tile it + 1 requested, indices of tile it + 2 loaded
+  __device__ __forceinline__ void next(const uint16_t* KV, const int32_t* idx_t, int L, int it, int ntiles,
+                                       int tid) {
+    if (it + 1 < ntiles) {
+      fetch(KV, tid);
+      if (it + 2 < ntiles) load_idx(idx_t, L, (it + 2) * sp::BK, tid);
     }
   }
 };
@@ -139,13 +162,12 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
   const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
-    gat.fetch(KV, idx_t, L, 0, tid);
-    gat.stash(smem, tid);
+    gat.start(KV, idx_t, L, ntiles, smem, tid);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int u0 = it * BK;
-    if (it + 1 < ntiles) gat.fetch(KV, idx_t, L, u0 + BK, tid);
+    gat.next(KV, idx_t, L, it, ntiles, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
 
     f32x4 s[2];
@@ -335,13 +357,12 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
   const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
-    gat.fetch(KV, idx_t, L, 0, tid);
-    gat.stash(smem, tid);
+    gat.start(KV, idx_t, L, ntiles, smem, tid);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int u0 = it * BK;
-    if (it + 1 < ntiles) gat.fetch(KV, idx_t, L, u0 + BK, tid);
+    gat.next(KV, idx_t, L, it, ntiles, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
     vec8 pb, db;
     recompute_p_ds<E>(kt, qreg, greg, rops, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
@@ -443,15 +464,14 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
   const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
-    gat.fetch(KV, idx_t, L, 0, tid);
-    gat.stash(smem, tid);
+    gat.start(KV, idx_t, L, ntiles, smem, tid);
   }
   __syncthreads();
   float* ws = a.dKVws;
   const float al = a.scale;
   for (int it = 0; it < ntiles; ++it) {
     const int u0 = it * BK;
-    if (it + 1 < ntiles) gat.fetch(KV, idx_t, L, u0 + BK, tid);
+    gat.next(KV, idx_t, L, it, ntiles, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
     vec8 pb, db;
     recompute_p_ds<E>(kt, qreg, greg, rops, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
