@@ -115,8 +115,8 @@ attn_status attn_fwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, in
                      float scale, int block_b, const attn_dropout_t* dropout,
                      void* Y, float* LSE, void* stream);
 
-/* Bytes of device workspace attn_bwd needs (fp32 D_i and the base-2 LSE of
- * every query row, plus padding). */
+/* Bytes of device workspace attn_bwd needs (fp32 D_i, stored negated, and the
+ * base-2 LSE of every query row, plus padding). */
 size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
                                int dv);
 
