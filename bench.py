@@ -292,7 +292,9 @@ def bench_sparse(w, args):
     LSE = torch.empty((w.Tq, w.H), dtype=torch.float32, device="cuda")
     dQ, dKV = gh.empty(Q.shape, w.dtype), gh.empty(KV.shape, w.dtype)
     dSink = torch.empty(w.H, dtype=torch.float32, device="cuda")
-    nb = ets.attn_sparse_bwd_workspace_size(w.Tq, w.H, w.Tkv, w.dqk, w.dv, w.topk)
+    det = bool(args.deterministic)
+    nb = (ets.attn_sparse_bwd_det_workspace_size if det else ets.attn_sparse_bwd_workspace_size)(
+        w.Tq, w.H, w.Tkv, w.dqk, w.dv, w.topk)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     shape = (dt, w.Tq, w.H, w.Tkv, w.dqk, w.dv, w.topk)
     stream = torch.cuda.current_stream()
@@ -301,8 +303,12 @@ def bench_sparse(w, args):
         ets.attn_sparse_fwd(*shape, Q, KV, idx, length, sink, w.alpha, O, LSE, stream=stream)
 
     def bwd():
-        ets.attn_sparse_bwd(*shape, Q, KV, idx, length, sink, w.alpha, O, LSE, dO, dQ, dKV, dSink, ws, nb,
-                            stream=stream)
+        if det:
+            ets.attn_sparse_bwd_det(ets.ATTN_LSE_TOTAL, *shape, Q, KV, idx, length, sink, w.alpha, O, LSE, dO, dQ,
+                                    dKV, dSink, ws, nb, stream=stream)
+        else:
+            ets.attn_sparse_bwd(*shape, Q, KV, idx, length, sink, w.alpha, O, LSE, dO, dQ, dKV, dSink, ws, nb,
+                                stream=stream)
 
     for _ in range(args.warmup):
         fwd()
@@ -331,7 +337,7 @@ def bench_sparse(w, args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1), workloads module)",
         "config": {"workload": w.name, "tokens": w.Tq, "heads": w.H, "kv_rows": w.Tkv, "d_qk": w.dqk, "d_v": w.dv,
-                   "topk": w.topk, "valid_pairs": pairs},
+                   "topk": w.topk, "valid_pairs": pairs, "deterministic_dkv": det},
         "fwd": {"ms": f_ms, "TFLOP/s": fl_f / (f_ms * 1e-3) / 1e12, "gathered_GB/s": fwd_gbs},
         "bwd": {"ms": b_ms, "TFLOP/s": fl_b / (b_ms * 1e-3) / 1e12,
                 "gathered_GB/s": 2 * gathered / (b_ms * 1e-3) / 1e9},
@@ -354,6 +360,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only the reference copy (counter scaling)")
     ap.add_argument("--no-dropout", action="store_true", help="dense workloads: run the same shape with rate 0")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="sparse workload: the bit-reproducible dKV backward (attn_sparse_bwd_det)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

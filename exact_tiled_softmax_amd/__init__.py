@@ -18,7 +18,7 @@ __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
     "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
-    "attn_sparse_fwd_lse", "attn_sparse_bwd_lse",
+    "attn_sparse_fwd_lse", "attn_sparse_bwd_lse", "attn_sparse_bwd_det", "attn_sparse_bwd_det_workspace_size",
     "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_status_string", "library_path", "lib",
 ]
 
@@ -96,6 +96,10 @@ lib.attn_sparse_fwd_lse.restype = _i
 lib.attn_sparse_fwd_lse.argtypes = [_i] + lib.attn_sparse_fwd.argtypes
 lib.attn_sparse_bwd_lse.restype = _i
 lib.attn_sparse_bwd_lse.argtypes = [_i] + lib.attn_sparse_bwd.argtypes
+lib.attn_sparse_bwd_det.restype = _i
+lib.attn_sparse_bwd_det.argtypes = [_i] + lib.attn_sparse_bwd.argtypes
+lib.attn_sparse_bwd_det_workspace_size.restype = _sz
+lib.attn_sparse_bwd_det_workspace_size.argtypes = [_i] * 6
 lib.attn_dropout_mask.restype = _i
 lib.attn_dropout_mask.argtypes = [_f, ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
 lib.attn_mfma_probe.restype = _i
@@ -223,6 +227,20 @@ def attn_sparse_bwd_lse(kind, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, 
                                  _ptr(dO), _ptr(dQ), _ptr(dKV), _ptr(dSink), _ptr(workspace),
                                  int(workspace_bytes), _stream(stream))
     return _check(st, "attn_sparse_bwd_lse", raise_on_error)
+
+
+def attn_sparse_bwd_det_workspace_size(Tq, H, Tkv, d_qk, d_v, topk):
+    return lib.attn_sparse_bwd_det_workspace_size(Tq, H, Tkv, d_qk, d_v, topk)
+
+
+def attn_sparse_bwd_det(kind, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                        O, LSE, dO, dQ, dKV, dSink, workspace, workspace_bytes, stream=None,
+                        raise_on_error=True):
+    st = lib.attn_sparse_bwd_det(int(kind), dt, Tq, H, Tkv, d_qk, d_v, topk, _ptr(Q), _ptr(KV), _ptr(topk_idx),
+                                 _ptr(topk_length), _ptr(attn_sink), float(scale), _ptr(O), _ptr(LSE),
+                                 _ptr(dO), _ptr(dQ), _ptr(dKV), _ptr(dSink), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
+    return _check(st, "attn_sparse_bwd_det", raise_on_error)
 
 
 def attn_dropout_mask(rate, seed, B, H, n_q, n_k, xi, stream=None, raise_on_error=True):

@@ -223,8 +223,14 @@ size_t attn_sparse_bwd_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v,
   return 2 * round_up((size_t)Tq * H * sizeof(float)) + round_up((size_t)Tkv * d_qk * sizeof(float));
 }
 
-attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
-                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+size_t attn_sparse_bwd_det_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk) {
+  (void)d_v; (void)topk;
+  if (bad_dims({Tq, H, Tkv, d_qk})) return 0;
+  return 2 * round_up((size_t)Tq * H * sizeof(float)) + round_up((size_t)Tkv * d_qk * sizeof(int64_t));
+}
+
+static attn_status sparse_bwd_common(int det, attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk,
+                                     int d_v, int topk, const void* Q, const void* KV, const int32_t* topk_idx,
                                 const int32_t* topk_length, const float* attn_sink, float scale,
                                 const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
                                 float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
@@ -238,18 +244,38 @@ attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H
   if (!aligned(topk_idx, 4) || !aligned(LSE, 4) || (topk_length && !aligned(topk_length, 4)) ||
       (attn_sink && !aligned(attn_sink, 4)) || (dSink && !aligned(dSink, 4)))
     return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk);
+  const size_t need = det ? attn_sparse_bwd_det_workspace_size(Tq, H, Tkv, d_qk, d_v, topk)
+                          : attn_sparse_bwd_workspace_size(Tq, H, Tkv, d_qk, d_v, topk);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return ATTN_ERR_WORKSPACE;
   SparseArgs a;
   fill_sparse(a, Tq, H, Tkv, d_qk, d_v, topk, scale);
   a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
   a.O = (void*)O; a.LSE = (float*)LSE; a.dO = dO; a.dQ = dQ; a.dKV = dKV; a.dSink = dSink;
   a.lse_kv = kind == ATTN_LSE_KV;
+  a.det = det;
   a.Dws = (float*)workspace;
   a.dsink_part = (float*)((char*)workspace + round_up((size_t)Tq * H * sizeof(float)));
   a.dKVws = (float*)((char*)workspace + 2 * round_up((size_t)Tq * H * sizeof(float)));
   const int rc = launch_sparse_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale,
+                                const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                                float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_bwd_common(0, kind, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                           O, LSE, dO, dQ, dKV, dSink, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_sparse_bwd_det(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale,
+                                const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                                float* dSink, void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_bwd_common(1, kind, dt, Tq, H, Tkv, d_qk, d_v, topk, Q, KV, topk_idx, topk_length, attn_sink, scale,
+                           O, LSE, dO, dQ, dKV, dSink, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_sparse_bwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,

@@ -55,6 +55,7 @@ struct SparseArgs {
   int Tq, H, Tkv, dqk, dv, topk;
   float scale, scale_log2;
   int lse_kv;        // 1: the LSE written / read covers the selected KV logits only (no sink)
+  int det;           // 1: dKVws holds int64 fixed point (units of 2^-32), summed with integer atomics
 };
 
 // Kernel launchers (defined in the .hip files).  Each returns 0 on success or

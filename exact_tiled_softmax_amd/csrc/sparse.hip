@@ -47,6 +47,12 @@ constexpr int SMEM = 2 * TILEB;
 constexpr float kRescaleSlack = 8.0f;
 }  // namespace sp
 
+// Deterministic dKV: each contribution is rounded to a multiple of 2^-32 and
+// added as a 64-bit integer, so the sum does not depend on the order of the
+// atomics (|dKV| must stay below 2^31).
+constexpr float kFix = 4294967296.0f;
+constexpr double kFixInv = 1.0 / 4294967296.0;
+
 bool sparse_supported(int H, int dqk, int dv) { return H == sp::H && dqk == sp::DQK && dv == sp::DV; }
 
 // Gather of one tile of selected rows (global -> registers -> LDS).  The row
@@ -270,7 +276,8 @@ __global__ __launch_bounds__(256) void sparse_bwd_prep_kernel(const SparseArgs a
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (lane == 0) a.Dws[row] = acc;
   }
-  const long long n4 = (long long)a.Tkv * sp::DQK / 4;
+  // the accumulator: fp32, or int64 fixed point in the deterministic mode
+  const long long n4 = (long long)a.Tkv * sp::DQK / 4 * (a.det ? 2 : 1);
   for (long long k = (long long)blockIdx.x * 256 + tid; k < n4; k += (long long)gridDim.x * 256)
     ((f32x4*)a.dKVws)[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
 }
 
 // dKV: contributions of one token, all 64 heads, into the fp32 accumulator
-template <class E>
+template <class E, bool DET>
 __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs a) {
   using namespace sp;
   typedef typename E::vec8 vec8;
@@ -520,7 +527,16 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
         const int col = c0w + 16 * m + l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (valid[r]) atomicAdd(ws + (size_t)jrow[r] * DQK + col, fmaf(acc[r], al, accv[r]));
+          if (valid[r]) {
+            const float v = fmaf(acc[r], al, accv[r]);
+            if constexpr (DET) {
+              // integer adds commute exactly: the sum is the same in any order
+              const long long q = __float2ll_rn(v * kFix);
+              atomicAdd((unsigned long long*)ws + (size_t)jrow[r] * DQK + col, (unsigned long long)q);
+            } else {
+              atomicAdd(ws + (size_t)jrow[r] * DQK + col, v);
+            }
+          }
       }
     }
     if (it + 1 < ntiles) gat.stash(smem + ((it + 1) & 1) * TILEB, tid);
@@ -529,12 +545,17 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
 }
 
 // dKV fp32 -> storage dtype; dSink[h] = sum over tokens (fixed order)
-template <class E>
+template <class E, bool DET>
 __global__ __launch_bounds__(256) void sparse_bwd_finalize_kernel(const SparseArgs a, const float* dsink_part) {
   const long long n2 = (long long)a.Tkv * sp::DQK / 2;
   for (long long k = (long long)blockIdx.x * 256 + threadIdx.x; k < n2; k += (long long)gridDim.x * 256) {
-    const f32x2 v = ((const f32x2*)a.dKVws)[k];
-    ((uint32_t*)a.dKV)[k] = E::pack2(v[0], v[1]);
+    if constexpr (DET) {
+      const long long* q = (const long long*)a.dKVws + 2 * k;
+      ((uint32_t*)a.dKV)[k] = E::pack2((float)((double)q[0] * kFixInv), (float)((double)q[1] * kFixInv));
+    } else {
+      const f32x2 v = ((const f32x2*)a.dKVws)[k];
+      ((uint32_t*)a.dKV)[k] = E::pack2(v[0], v[1]);
+    }
   }
   if (a.sink && blockIdx.x < sp::H) {
     __shared__ float red[256];
@@ -565,12 +586,14 @@ static int launch_bwd_e(const SparseArgs& a, hipStream_t st) {
   const int prep_blocks = (a.Tq * sp::H + 3) / 4;
   ETS_TRY(launch(sparse_bwd_prep_kernel<E>, dim3(prep_blocks), dim3(256), 0, st, a));
   ETS_TRY(launch(sparse_bwd_dq_kernel<E>, dim3(a.Tq), dim3(256), sp::SMEM, st, a, dsink_part));
-  ETS_TRY(launch(sparse_bwd_dkv_kernel<E>, dim3(a.Tq), dim3(256), SMEM_DKV, st, a));
+  if (a.det) ETS_TRY(launch(sparse_bwd_dkv_kernel<E, true>, dim3(a.Tq), dim3(256), SMEM_DKV, st, a));
+  else ETS_TRY(launch(sparse_bwd_dkv_kernel<E, false>, dim3(a.Tq), dim3(256), SMEM_DKV, st, a));
   const long long n2 = (long long)a.Tkv * sp::DQK / 2;
   long long blocks = (n2 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < sp::H) blocks = sp::H;
-  ETS_TRY(launch(sparse_bwd_finalize_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st, a, dsink_part));
+  if (a.det) ETS_TRY(launch(sparse_bwd_finalize_kernel<E, true>, dim3((unsigned)blocks), dim3(256), 0, st, a, dsink_part));
+  else ETS_TRY(launch(sparse_bwd_finalize_kernel<E, false>, dim3((unsigned)blocks), dim3(256), 0, st, a, dsink_part));
   return 0;
 }
 

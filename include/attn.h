@@ -242,6 +242,28 @@ attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H
                                 const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
                                 float* dSink, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_sparse_bwd_det needs (as
+ * attn_sparse_bwd_workspace_size, with a 64-bit [Tkv][d_qk] accumulator). */
+size_t attn_sparse_bwd_det_workspace_size(int Tq, int H, int Tkv, int d_qk, int d_v, int topk);
+
+/*
+ * attn_sparse_bwd_det -- attn_sparse_bwd_lse with a bit-reproducible dKV
+ * ([P5] section 9 notes that fp32 atomics make dKV order dependent; here the
+ * order stops mattering instead of being fixed): every contribution
+ * alpha dS_u q + p_u dO to
+ * dKV[I_u] is rounded to a multiple of 2^-32 and added as a 64-bit integer, so
+ * the total is the same for any order of the additions and dKV is bit
+ * reproducible from run to run; it is converted to fp32 and then rounded once
+ * to the storage dtype.  Requires |dKV| < 2^31 element-wise.  dQ and dSink
+ * are as attn_sparse_bwd (already deterministic).  The workspace must hold
+ * attn_sparse_bwd_det_workspace_size() bytes.
+ */
+attn_status attn_sparse_bwd_det(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,
+                                int topk, const void* Q, const void* KV, const int32_t* topk_idx,
+                                const int32_t* topk_length, const float* attn_sink, float scale,
+                                const void* O, const float* LSE, const void* dO, void* dQ, void* dKV,
+                                float* dSink, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * attn_dropout_mask -- writes the dropout realisation xi that attn_fwd and
  * attn_bwd use (see attn_dropout_t) as uint8 [B][H][n_q][n_k] (1 = kept), for

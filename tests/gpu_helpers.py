@@ -96,9 +96,10 @@ def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=
     return res
 
 
-def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None, lse_kind=None):
+def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None, lse_kind=None, det=False):
     """Run attn_sparse_fwd (and attn_sparse_bwd when dO is given); with
-    lse_kind, the _lse entry points in that LSE convention."""
+    lse_kind, the _lse entry points in that LSE convention; with det, the
+    deterministic backward."""
     import exact_tiled_softmax_amd as ets
     torch = torch_cuda()
     Tq, H, dqk = Q.shape
@@ -121,9 +122,13 @@ def sparse_run(dtype, Q, KV, idx, length, sink, scale, dO=None, lse_kind=None):
         g = to_dev(dO, dtype)
         dQ, dKV = empty(Q.shape, dtype), empty(KV.shape, dtype)
         dSink = torch.zeros(H, dtype=torch.float32, device="cuda") if sink is not None else None
-        nb = ets.attn_sparse_bwd_workspace_size(Tq, H, Tkv, dqk, dv, topk)
+        nb = (ets.attn_sparse_bwd_det_workspace_size if det else ets.attn_sparse_bwd_workspace_size)(
+            Tq, H, Tkv, dqk, dv, topk)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        if lse_kind is None:
+        if det:
+            ets.attn_sparse_bwd_det(ets.ATTN_LSE_TOTAL if lse_kind is None else lse_kind, dt, Tq, H, Tkv, dqk, dv,
+                                    topk, q, kv, di, dl, ds, scale, O, LSE, g, dQ, dKV, dSink, ws, nb)
+        elif lse_kind is None:
             ets.attn_sparse_bwd(dt, Tq, H, Tkv, dqk, dv, topk, q, kv, di, dl, ds, scale, O, LSE, g, dQ, dKV, dSink,
                                 ws, nb)
         else:

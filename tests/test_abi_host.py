@@ -47,6 +47,7 @@ def test_workspace_sizes():
     assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 4, 16, 16, 2048, 2048, 128, 128) == 2 * (((4 * 16 * 2048 + 64) * 4 + 255) // 256 * 256)
     assert ets.attn_bwd_workspace_size(ets.ATTN_BF16, 0, 16, 16, 2048, 2048, 128, 128) == 0
     assert ets.attn_sparse_bwd_workspace_size(4096, 64, 16384, 576, 512, 2048) == 2 * 4096 * 64 * 4 + 16384 * 576 * 4
+    assert ets.attn_sparse_bwd_det_workspace_size(4096, 64, 16384, 576, 512, 2048) == 2 * 4096 * 64 * 4 + 16384 * 576 * 8
 
 
 P = 0x10000  # a dummy aligned address: never dereferenced, every call fails validation
@@ -117,6 +118,19 @@ def test_sparse_lse_kind_is_checked_before_launch():
     assert ets.attn_sparse_bwd_lse(ets.ATTN_LSE_KV, ets.ATTN_BF16, 8, 64, 32, 576, 512, 16, P, P, P, None, None,
                                    0.04, P, P, P, P, P, None, None, need, stream=0,
                                    raise_on_error=False) == ets.ATTN_ERR_WORKSPACE
+
+
+def test_sparse_deterministic_backward_needs_its_larger_workspace():
+    import exact_tiled_softmax_amd as ets
+    small = ets.attn_sparse_bwd_workspace_size(8, 64, 32, 576, 512, 16)
+    need = ets.attn_sparse_bwd_det_workspace_size(8, 64, 32, 576, 512, 16)
+    assert need > small
+    st = ets.attn_sparse_bwd_det(ets.ATTN_LSE_TOTAL, ets.ATTN_BF16, 8, 64, 32, 576, 512, 16, P, P, P, None, None,
+                                 0.04, P, P, P, P, P, None, P, need - 1, stream=0, raise_on_error=False)
+    assert st == ets.ATTN_ERR_WORKSPACE
+    st = ets.attn_sparse_bwd_det(5, ets.ATTN_BF16, 8, 64, 32, 576, 512, 16, P, P, P, None, None,
+                                 0.04, P, P, P, P, P, None, P, need, stream=0, raise_on_error=False)
+    assert st == ets.ATTN_ERR_INVALID_ARG
 
 
 def test_dropout_mask_rejects_bad_rate():

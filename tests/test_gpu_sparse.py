@@ -127,3 +127,19 @@ def test_sparse_kv_only_lse_export_and_backward(sink):
         assert np.array_equal(r["LSE"], ref["LSE"])  # without a sink the conventions coincide
         assert np.array_equal(r["dQ"], ref["dQ"])
 
+
+def test_sparse_deterministic_dkv_is_bit_reproducible():
+    # [P5] section 9: fp32 atomics make dKV depend on the order of the adds; the
+    # deterministic mode sums fixed-point integers, so two runs agree bit for bit
+    c = _case(40, 300, 120, "bf16", 6, dup=True)
+    alpha = 1.0 / 24.0
+    sink64 = c["sink"].astype(np.float64)
+    r1 = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=c["dO"], det=True)
+    r2 = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=c["dO"], det=True)
+    ref = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=c["dO"])
+    assert np.array_equal(r1["dKV"], r2["dKV"])
+    assert np.array_equal(r1["dQ"], ref["dQ"]) and np.array_equal(r1["dSink"], ref["dSink"])
+    _, dKV, _ = sparse.vjp(c["Q64"], c["KV64"], c["idx"], c["L"], sink64, alpha, DV, c["dO64"])
+    assert gh.rel_fro(r1["dKV"], dKV) <= REL_TOL
+    assert gh.rel_fro(r1["dKV"], ref["dKV"]) <= 1e-2
+
