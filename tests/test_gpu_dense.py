@@ -270,3 +270,29 @@ def test_mfma_probe_runs_and_counts():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert n == cus * 8 * 8 * 8
     assert bool(torch.isfinite(sink[:cus]).all())
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_backward_phases_reproduce_attn_bwd(dtype, d):
+    # attn_bwd_phase(1), (2), (4) in turn run the same kernels on the same
+    # workspace as attn_bwd, so the gradients agree bit for bit
+    import exact_tiled_softmax_amd as ets
+    torch = gh.torch_cuda()
+    n = 333
+    a = _inputs(1, 4, 2, n, d, d, dtype, 77)
+    c = 1.0 / math.sqrt(d)
+    mask = gh.mask_arg(causal=True, window=200)
+    r = gh.dense_run(dtype, a["Q"], a["K"], a["V"], a["G"], mask, c)
+    dev = r["_dev"]
+    dt = gh.DT[dtype]
+    shape = (dt, 1, 4, 2, n, n, d, d)
+    q, k, v, g = (gh.to_dev(a[x], dtype) for x in ("Q", "K", "V", "G"))
+    dQ, dK, dV = gh.empty(a["Q"].shape, dtype), gh.empty(a["K"].shape, dtype), gh.empty(a["V"].shape, dtype)
+    nb = ets.attn_bwd_workspace_size(*shape)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for ph in (1, 2, 4):
+        ets.attn_bwd_phase(ph, *shape, q, k, v, dev["Y"], dev["LSE"], g, mask, c, 0, None, dQ, dK, dV, ws, nb)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        assert np.array_equal(gh.from_dev(t, dtype), r[name]), name
+
