@@ -41,6 +41,18 @@ Grouped heads: query head h reads K/V head h // (H / H_kv), the adjacent group
 map of the course's multi-head layer (intale.github.io ch. 19, "Change
 attention evaluation inside the existing model"); the key and value gradients
 of every query head in a group add into the shared head.
+
+Variable lengths and packed segments (intale.github.io ch. 19: "Change
+attention evaluation inside the existing model" intersects the causal range
+with each sequence's active length and with packed-segment boundaries; the
+update-rule listing under "Rescale earlier mass before adding a new tile"
+reads a per-(batch, query row) lower key bound, its `starts`, and that
+section's closing paragraph keeps inactive padded rows at zero with no
+division).  Two more parts of the allowed set, per batch b:
+  lengths[b]      rows i >= lengths[b] are inactive (empty allowed set) and
+                  keys j >= lengths[b] are never allowed;
+  starts[b, i]    keys j < starts[b, i] are not allowed for row i (for packed
+                  segments: the first row of the segment holding row i).
 """
 
 import numpy as np
@@ -58,20 +70,25 @@ class Allowed:
                                            the window keys include self)
     block_mask  block_mask[i // block_q, j // block_k] != 0
     dense_mask  dense_mask[i, j] != 0
-    With no part enabled every key is allowed.
+    lengths     per batch b: i < lengths[b] and j < lengths[b]
+    starts      per batch b: j >= starts[b, i]
+    With no part enabled every key is allowed.  Only lengths and starts
+    depend on the batch index.
     """
 
     def __init__(self, n_q, n_k, causal=False, window=0, block_mask=None,
-                 block_q=64, block_k=64, dense_mask=None):
+                 block_q=64, block_k=64, dense_mask=None, lengths=None, starts=None):
         self.n_q, self.n_k = int(n_q), int(n_k)
         self.causal = bool(causal)
         self.window = int(window)
         self.block_mask = None if block_mask is None else np.asarray(block_mask) != 0
         self.block_q, self.block_k = int(block_q), int(block_k)
         self.dense_mask = None if dense_mask is None else np.asarray(dense_mask) != 0
+        self.lengths = None if lengths is None else np.asarray(lengths, dtype=np.int64)
+        self.starts = None if starts is None else np.asarray(starts, dtype=np.int64)
 
-    def rows(self, rows):
-        """bool [len(rows), n_k] for the given query row indices."""
+    def rows(self, rows, b=0):
+        """bool [len(rows), n_k] for the given query row indices of batch b."""
         i = np.asarray(rows, dtype=np.int64)[:, None]
         j = np.arange(self.n_k, dtype=np.int64)[None, :]
         a = np.ones((i.shape[0], self.n_k), dtype=bool)
@@ -83,14 +100,19 @@ class Allowed:
             a &= self.block_mask[i // self.block_q, j // self.block_k]
         if self.dense_mask is not None:
             a &= self.dense_mask[i[:, 0], :]
+        if self.lengths is not None:
+            n_active = int(self.lengths[b])
+            a &= (i < n_active) & (j < n_active)
+        if self.starts is not None:
+            a &= j >= self.starts[b][i[:, 0]][:, None]
         return a
 
-    def pair_count(self):
-        """|A| = sum_i |A_i| (the number of allowed (i, j) pairs)."""
+    def pair_count(self, b=0):
+        """|A| = sum_i |A_i| (the number of allowed (i, j) pairs) of batch b."""
         total = 0
         step = max(1, _ROW_BUDGET // max(1, self.n_k))
         for i0 in range(0, self.n_q, step):
-            total += int(self.rows(np.arange(i0, min(self.n_q, i0 + step))).sum())
+            total += int(self.rows(np.arange(i0, min(self.n_q, i0 + step)), b).sum())
         return total
 
 
@@ -149,7 +171,7 @@ def forward_rows(Q, K, V, allowed, c, b, h, rows, dropout=None):
     step = max(1, _ROW_BUDGET // max(1, k.shape[0]))
     for s0 in range(0, rows.size, step):
         r = rows[s0:s0 + step]
-        p, m, l = _row_probabilities(np.asarray(Q[b, h, r], dtype=np.float64), k, c, allowed.rows(r))
+        p, m, l = _row_probabilities(np.asarray(Q[b, h, r], dtype=np.float64), k, c, allowed.rows(r, b))
         w = p if dropout is None else p * dropout.kappa(b, h, H, r, k.shape[0])
         Y[s0:s0 + step] = w @ v
         LSE[s0:s0 + step] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
@@ -188,7 +210,7 @@ def vjp_lane(Q, K, V, allowed, c, G, b, h, dropout=None, rows=None):
         r = rows[s0:s0 + step]
         q = np.asarray(Q[b, h, r], dtype=np.float64)
         gr = np.asarray(G[b, h, r], dtype=np.float64)
-        p, _, _ = _row_probabilities(q, k, c, allowed.rows(r))
+        p, _, _ = _row_probabilities(q, k, c, allowed.rows(r, b))
         kap = None if dropout is None else dropout.kappa(b, h, H, r, k.shape[0])
         w = p if kap is None else p * kap
         y = w @ v

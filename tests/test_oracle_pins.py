@@ -431,3 +431,143 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(bits, ref)
     np.testing.assert_array_equal(workloads.bf16_bits_to_f64(bits),
                                   torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+# ------------------------------------------------------------ allowed sets
+# The parts of A_i other than causal are pinned here against hand-enumerated
+# sets and closed-form counts, so that a slip in a comparison (< vs <=), a
+# swapped block_q / block_k or a per-batch index mistake fails.
+
+
+def test_window_and_tile_mask_sets_hand_enumerated():
+    # n = 6, causal, look-back window 3 (i - j < 3), tile mask on 2-row x 3-key
+    # tiles [[1, 0], [0, 1], [1, 1]]: rows {0,1} keep keys {0,1,2}, rows {2,3}
+    # keep keys {3,4,5}, rows {4,5} keep every key
+    bm = np.array([[1, 0], [0, 1], [1, 1]], np.uint8)
+    A = dense.Allowed(6, 6, causal=True, window=3, block_mask=bm, block_q=2, block_k=3)
+    want = [[0], [0, 1], [], [3], [2, 3, 4], [3, 4, 5]]
+    got = A.rows(np.arange(6))
+    for i in range(6):
+        assert np.flatnonzero(got[i]).tolist() == want[i], i
+    # the window alone (no causal): keys j with i - j < 3, including every later key
+    Aw = dense.Allowed(4, 4, window=3)
+    assert [np.flatnonzero(r).tolist() for r in Aw.rows(np.arange(4))] == [[0, 1, 2, 3], [0, 1, 2, 3],
+                                                                          [0, 1, 2, 3], [1, 2, 3]]
+
+
+@pytest.mark.parametrize("n,W", [(1, 1), (7, 3), (64, 64), (200, 37), (333, 256), (4096, 256)])
+def test_causal_window_pair_count_closed_form(n, W):
+    # sum_i min(i + 1, W) = W (W + 1) / 2 + (n - W) W for n >= W, else n (n + 1) / 2
+    want = W * (W + 1) // 2 + (n - W) * W if n >= W else n * (n + 1) // 2
+    assert dense.Allowed(n, n, causal=True, window=W).pair_count() == want
+
+
+def test_causal_tile_mask_pair_count_closed_form():
+    # with T x T tiles a kept diagonal tile holds T (T + 1) / 2 causal pairs and
+    # a kept tile below the diagonal T^2; tiles above the diagonal hold none
+    rng = np.random.default_rng(30)
+    T, nt = 5, 7
+    bm = (rng.random((nt, nt)) < 0.5).astype(np.uint8)
+    want = sum(int(bm[r, c]) * (T * T if r > c else (T * (T + 1) // 2 if r == c else 0))
+               for r in range(nt) for c in range(nt))
+    assert dense.Allowed(T * nt, T * nt, causal=True, block_mask=bm, block_q=T, block_k=T).pair_count() == want
+    # rectangular tiles: only the row index is divided by block_q
+    bq, bk = 2, 4
+    bm2 = np.zeros((4, 2), np.uint8)
+    bm2[1, 0] = 1   # rows 2, 3 x keys 0..3
+    bm2[3, 1] = 1   # rows 6, 7 x keys 4..7
+    A2 = dense.Allowed(8, 8, block_mask=bm2, block_q=bq, block_k=bk)
+    assert A2.pair_count() == 16
+    assert np.flatnonzero(A2.rows([6])[0]).tolist() == [4, 5, 6, 7]
+    assert not A2.rows([4])[0].any()
+
+
+def test_bench_pair_count_agrees_with_closed_forms():
+    import bench
+    import workloads
+    for name, w in workloads.WORKLOADS.items():
+        if not isinstance(w, workloads.DenseWorkload) or w.n > 4096:
+            continue
+        bm = workloads.dense_arrays(w)["block_mask"]
+        A = dense.Allowed(w.n, w.n, causal=w.causal, window=w.window, block_mask=bm,
+                          block_q=w.mask_tile, block_k=w.mask_tile)
+        assert bench.dense_pairs(w, bm) == A.pair_count(), name
+    w = workloads.WORKLOADS["dense_causal_bf16_b4h16_n2048_d128"]
+    assert bench.dense_pairs(w, None) == 2048 * 2049 // 2
+
+
+def test_lengths_and_starts_sets_hand_enumerated():
+    # batch 0: active length 4 of n = 5, no starts effect; batch 1: two packed
+    # segments [0, 2) and [2, 5) (starts = segment starts), causal
+    starts = np.array([[0, 0, 0, 0, 0], [0, 0, 2, 2, 2]])
+    A = dense.Allowed(5, 5, causal=True, lengths=[4, 5], starts=starts)
+    got0 = [np.flatnonzero(r).tolist() for r in A.rows(np.arange(5), b=0)]
+    got1 = [np.flatnonzero(r).tolist() for r in A.rows(np.arange(5), b=1)]
+    assert got0 == [[0], [0, 1], [0, 1, 2], [0, 1, 2, 3], []]
+    assert got1 == [[0], [0, 1], [2], [2, 3], [2, 3, 4]]
+    # a lower bound above the row itself empties a causal row; without causal
+    # the keys past the active length stay excluded
+    A2 = dense.Allowed(4, 4, lengths=[3], starts=[[1, 3, 0, 0]])
+    assert [np.flatnonzero(r).tolist() for r in A2.rows(np.arange(4))] == [[1, 2], [], [0, 1, 2], []]
+    assert A.pair_count(0) == 10 and A.pair_count(1) == 1 + 2 + 1 + 2 + 3
+
+
+def test_inactive_rows_reduce_to_the_unpadded_sequence():
+    # lengths[b] = L: the first L rows equal attention over the L-token
+    # sequence alone; inactive rows are zero with LSE -inf and add nothing to
+    # any gradient (the course's inactive padded rows)
+    rng = np.random.default_rng(31)
+    n, d, dv, L = 9, 3, 2, 6
+    Q, K, V, G = _rand((2, 1, n, d), rng), _rand((2, 1, n, d), rng), _rand((2, 1, n, dv), rng), _rand((2, 1, n, dv), rng)
+    A = dense.Allowed(n, n, causal=True, lengths=[L, n])
+    Y, LSE = dense.forward(Q, K, V, A, 0.7)
+    dQ, dK, dV = dense.vjp(Q, K, V, A, 0.7, G)
+    sl = slice(0, L)
+    Ys, LSEs = dense.forward(Q[:1, :, sl], K[:1, :, sl], V[:1, :, sl], dense.Allowed(L, L, causal=True), 0.7)
+    dQs, dKs, dVs = dense.vjp(Q[:1, :, sl], K[:1, :, sl], V[:1, :, sl], dense.Allowed(L, L, causal=True), 0.7,
+                              G[:1, :, sl])
+    np.testing.assert_allclose(Y[0, 0, sl], Ys[0, 0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(LSE[0, 0, sl], LSEs[0, 0], rtol=1e-13)
+    assert np.all(Y[0, 0, L:] == 0) and np.all(np.isneginf(LSE[0, 0, L:]))
+    for full, short in ((dQ, dQs), (dK, dKs), (dV, dVs)):
+        np.testing.assert_allclose(full[0, 0, sl], short[0, 0], rtol=1e-12, atol=1e-13)
+        assert np.all(full[0, 0, L:] == 0)
+    # batch 1 is untouched by batch 0's length
+    Yf, _ = dense.forward(Q[1:], K[1:], V[1:], dense.Allowed(n, n, causal=True), 0.7)
+    np.testing.assert_allclose(Y[1], Yf[0], rtol=1e-13, atol=1e-14)
+
+
+def test_packed_segments_reduce_to_separate_sequences():
+    # causal attention over packed segments (starts = first row of each row's
+    # segment) equals causal attention over each segment on its own
+    rng = np.random.default_rng(32)
+    segs = [4, 1, 6, 3]
+    n, d, dv = sum(segs), 4, 3
+    Q, K, V, G = _rand((1, 2, n, d), rng), _rand((1, 1, n, d), rng), _rand((1, 1, n, dv), rng), _rand((1, 2, n, dv), rng)
+    starts = np.concatenate([np.full(s, o) for s, o in zip(segs, np.cumsum([0] + segs[:-1]))])[None]
+    A = dense.Allowed(n, n, causal=True, starts=starts)
+    Y, LSE = dense.forward(Q, K, V, A, 0.6)
+    dQ, dK, dV = dense.vjp(Q, K, V, A, 0.6, G)
+    o = 0
+    for s in segs:
+        sl = slice(o, o + s)
+        As = dense.Allowed(s, s, causal=True)
+        Ys, LSEs = dense.forward(Q[:, :, sl], K[:, :, sl], V[:, :, sl], As, 0.6)
+        dQs, dKs, dVs = dense.vjp(Q[:, :, sl], K[:, :, sl], V[:, :, sl], As, 0.6, G[:, :, sl])
+        np.testing.assert_allclose(Y[:, :, sl], Ys, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(LSE[:, :, sl], LSEs, rtol=1e-13)
+        for full, short in ((dQ, dQs), (dK, dKs), (dV, dVs)):
+            np.testing.assert_allclose(full[:, :, sl], short, rtol=1e-12, atol=1e-13)
+        o += s
+
+
+def test_layout_vjp_matches_finite_differences():
+    rng = np.random.default_rng(33)
+    n, d, dv = 6, 3, 2
+    Q, K, V, G = _rand((2, 1, n, d), rng), _rand((2, 1, n, d), rng), _rand((2, 1, n, dv), rng), _rand((2, 1, n, dv), rng)
+    starts = np.array([[0, 0, 1, 1, 3, 3], [0, 1, 1, 2, 2, 5]])
+    A = dense.Allowed(n, n, causal=True, lengths=[5, 6], starts=starts)
+    dQ, dK, dV = dense.vjp(Q, K, V, A, 0.8, G)
+    num = fd.gradient(_phi_dense(A, 0.8, None), [Q, K, V, G])
+    for a, b in zip((dQ, dK, dV), num[:3]):
+        np.testing.assert_allclose(a, b, rtol=0, atol=4e-6)
