@@ -16,13 +16,14 @@ import os
 
 __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
+    "ATTN_ERR_NONFINITE",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
     "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_fwd_lse", "attn_sparse_bwd_lse", "attn_sparse_bwd_det", "attn_sparse_bwd_det_workspace_size",
     "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_status_string", "library_path", "lib",
 ]
 
-ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP, ATTN_ERR_NONFINITE = range(6)
 ATTN_F32, ATTN_F16, ATTN_BF16 = range(3)
 ATTN_LSE_TOTAL, ATTN_LSE_KV = range(2)
 
@@ -62,10 +63,12 @@ lib = ctypes.CDLL(library_path)
 
 
 class Mask(ctypes.Structure):
-    """attn_mask_t: causal, window, block_mask (device ptr), block_q, block_k, dense_mask (device ptr)."""
+    """attn_mask_t: causal, window, block_mask (device ptr), block_q, block_k, dense_mask,
+    lengths and starts (device ptrs)."""
     _fields_ = [("causal", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("block_mask", ctypes.c_void_p), ("block_q", ctypes.c_int32),
-                ("block_k", ctypes.c_int32), ("dense_mask", ctypes.c_void_p)]
+                ("block_k", ctypes.c_int32), ("dense_mask", ctypes.c_void_p),
+                ("lengths", ctypes.c_void_p), ("starts", ctypes.c_void_p)]
 
 
 class Dropout(ctypes.Structure):
@@ -139,7 +142,8 @@ def _mask(m):
         return ctypes.byref(m)
     d = dict(m)
     return ctypes.byref(Mask(int(d.get("causal", 0)), int(d.get("window", 0)), _ptr(d.get("block_mask")),
-                             int(d.get("block_q", 0)), int(d.get("block_k", 0)), _ptr(d.get("dense_mask"))))
+                             int(d.get("block_q", 0)), int(d.get("block_k", 0)), _ptr(d.get("dense_mask")),
+                             _ptr(d.get("lengths")), _ptr(d.get("starts"))))
 
 
 def _drop(d):

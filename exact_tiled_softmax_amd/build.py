@@ -3,8 +3,11 @@
 Usage: python exact_tiled_softmax_amd/build.py [-v]   (runs without importing the package)
 
 Each source is compiled to an object under <repo>/_build/ (in parallel), then
-linked into exact_tiled_softmax_amd/libattn.so next to this file.  Packed fp32
-vector instructions are disabled for all device code.
+linked into exact_tiled_softmax_amd/libattn.so next to this file.  The dense
+MFMA kernels (dense_fwd.hip, dense_dkdv.hip, dense_dq.hip) are compiled once
+per (dtype, head width) with -DETS_DT / -DETS_D, so that their instantiations
+build in parallel.  Packed fp32 vector instructions are disabled for all device
+code.
 """
 
 import concurrent.futures
@@ -19,7 +22,14 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "dense_fwd.hip", "dense_bwd.hip", "dense_f32.hip", "dropout.hip", "sparse.hip", "probe.hip"]
+_PER_COMBO = ["dense_fwd.hip", "dense_dkdv.hip", "dense_dq.hip"]
+_COMBOS = [(2, 128), (2, 64), (1, 128), (1, 64)]  # (dtype code: 2 = bf16, 1 = fp16; head width)
+# (source, extra defines, object name), slowest first
+UNITS = ([(src, [f"-DETS_DT={dt}", f"-DETS_D={d}"], f"{src[:-4]}_{dt}_{d}.o")
+          for src in _PER_COMBO for dt, d in _COMBOS] +
+         [(src, [], src.rsplit(".", 1)[0] + ".o")
+          for src in ("sparse.hip", "dense_bwd.hip", "dense_f32.hip", "abi.cpp", "dropout.hip", "probe.hip",
+                     "debug.hip")])
 
 ARCH = "gfx950"
 FLAGS = [
@@ -38,9 +48,10 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP kernels)")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit, verbose):
+    src, defines, objname = unit
+    obj = os.path.join(BUILD, objname)
+    cmd = [hipcc()] + FLAGS + defines + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")
@@ -57,8 +68,9 @@ def _compile(src, verbose):
 def build(verbose=False):
     """Compile every source and link libattn.so.  Always recompiles."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    workers = max(1, min(len(UNITS), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

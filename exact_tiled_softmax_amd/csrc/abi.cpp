@@ -4,6 +4,7 @@
 // include/attn.h.
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/attn.h"
@@ -14,6 +15,19 @@ using namespace ets;
 namespace {
 
 constexpr int kMaxF32Width = 128;
+// Index arithmetic limits of the kernels: 32-bit buffer-resource extents per
+// (batch, head) tensor, 32-bit offsets into the backward workspace, and the
+// 65535 (batch, head) lanes of the fp32 path's second grid dimension.
+constexpr long long kMaxHeadBytes = (1LL << 32) - 1;
+constexpr long long kMaxRows = (1LL << 28) - 64;
+constexpr long long kMaxF32Lanes = 65535;
+
+// Debug checks for this call: the environment variable ATTN_DEBUG holds a
+// nonzero integer.
+bool debug_enabled() {
+  const char* v = std::getenv("ATTN_DEBUG");
+  return v && std::strtol(v, nullptr, 10) != 0;
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -40,16 +54,25 @@ attn_status check_dense(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k,
     if (mask->causal && n_q != n_k) return ATTN_ERR_INVALID_ARG;
     if (mask->window < 0) return ATTN_ERR_INVALID_ARG;
     if (mask->block_mask && (mask->block_q < 1 || mask->block_k < 1)) return ATTN_ERR_INVALID_ARG;
+    if (mask->lengths && n_q != n_k) return ATTN_ERR_INVALID_ARG;
+    if ((mask->lengths && !aligned(mask->lengths, 4)) || (mask->starts && !aligned(mask->starts, 4)))
+      return ATTN_ERR_INVALID_ARG;
   }
   if (drop) {
     if (!std::isfinite(drop->rate) || drop->rate < 0.f || drop->rate >= 1.f) return ATTN_ERR_INVALID_ARG;
   }
   if (dt == ATTN_F32) {
     if (d > kMaxF32Width || dv > kMaxF32Width) return ATTN_ERR_UNSUPPORTED;
+    if ((long long)B * H > kMaxF32Lanes) return ATTN_ERR_UNSUPPORTED;
   } else {
     if (!dense_mfma_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
     if (block_b != 0 && block_b != 64) return ATTN_ERR_UNSUPPORTED;
   }
+  const long long esz = dt == ATTN_F32 ? 4 : 2;
+  if ((long long)n_q * d * esz > kMaxHeadBytes || (long long)n_k * d * esz > kMaxHeadBytes ||
+      (long long)n_q * dv * esz > kMaxHeadBytes || (long long)n_k * dv * esz > kMaxHeadBytes)
+    return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * H * n_q > kMaxRows || (long long)B * H_kv * n_k > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -68,6 +91,9 @@ void fill_dense(DenseArgs& a, attn_dtype dt, int B, int H, int H_kv, int n_q, in
     a.mask.bk = mask->block_mask ? mask->block_k : 1;
     a.mask.nbk = mask->block_mask ? (n_k + mask->block_k - 1) / mask->block_k : 0;
     a.mask.dense_mask = mask->dense_mask;
+    a.mask.dm_stride = n_k;
+    a.mask.lengths = mask->lengths;
+    a.mask.starts = mask->starts;
   }
   if (drop && drop->rate > 0.f) {
     const double r = (double)drop->rate;
@@ -79,7 +105,23 @@ void fill_dense(DenseArgs& a, attn_dtype dt, int B, int H, int H_kv, int n_q, in
   }
 }
 
-size_t elem_bytes(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
+// Debug scan kind of a tensor of dtype dt (see DebugBuf)
+int kind_of(attn_dtype dt) { return dt == ATTN_F32 ? 0 : (dt == ATTN_F16 ? 1 : 2); }
+
+// Debug checks: lengths within [0, n] before a dense launch; non-finite
+// outputs after one.
+attn_status debug_check_mask(const attn_mask_t* mask, int B, int n, void* stream) {
+  if (!mask || !mask->lengths) return ATTN_OK;
+  int bad = 0;
+  if (debug_check_lengths(mask->lengths, B, n, stream, &bad) != 0) return ATTN_ERR_HIP;
+  return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
+}
+
+attn_status debug_scan(const DebugBuf* bufs, int n, void* stream) {
+  int bad = 0;
+  if (debug_scan_nonfinite(bufs, n, stream, &bad) != 0) return ATTN_ERR_HIP;
+  return bad ? ATTN_ERR_NONFINITE : ATTN_OK;
+}
 
 }  // namespace
 
@@ -92,6 +134,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch failed";
+    case ATTN_ERR_NONFINITE: return "non-finite value in an output (debug check)";
   }
   return "unknown status";
 }
@@ -106,12 +149,23 @@ attn_status attn_fwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, in
   const size_t al = dt == ATTN_F32 ? 4 : 16;
   if (!aligned(Q, al) || !aligned(K, al) || !aligned(V, al) || !aligned(Y, al) || !aligned(LSE, 4))
     return ATTN_ERR_INVALID_ARG;
+  const bool dbg = debug_enabled();
+  if (dbg) {
+    const attn_status cs = debug_check_mask(mask, B, n_q, stream);
+    if (cs != ATTN_OK) return cs;
+  }
   DenseArgs a;
   fill_dense(a, dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
   a.Q = Q; a.K = K; a.V = V; a.out_Y = Y; a.LSE = LSE;
   const int rc = dt == ATTN_F32 ? launch_dense_fwd_f32(a, stream)
                                 : launch_dense_fwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
-  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+  if (rc != 0) return ATTN_ERR_HIP;
+  if (dbg) {
+    const long long rows = (long long)B * H * n_q;
+    const DebugBuf bufs[2] = {{Y, rows * dv, kind_of(dt)}, {LSE, rows, 3}};
+    return debug_scan(bufs, 2, stream);
+  }
+  return ATTN_OK;
 }
 
 size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
@@ -141,6 +195,11 @@ static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv,
   if (LSE && !aligned(LSE, 4)) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  const bool dbg = debug_enabled();
+  if (dbg) {
+    const attn_status cs = debug_check_mask(mask, B, n_q, stream);
+    if (cs != ATTN_OK) return cs;
+  }
   DenseArgs a;
   fill_dense(a, dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
   a.Q = Q; a.K = K; a.V = V; a.Y = Y; a.LSE = (float*)LSE; a.G = G;
@@ -148,7 +207,15 @@ static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv,
   a.Lws = (float*)((char*)workspace + round_up(((size_t)B * H * n_q + 64) * sizeof(float)));
   const int rc = dt == ATTN_F32 ? launch_dense_bwd_f32(a, stream, phases)
                                 : launch_dense_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream, phases);
-  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+  if (rc != 0) return ATTN_ERR_HIP;
+  if (dbg && (phases & 6)) {
+    const int k = kind_of(dt);
+    const DebugBuf bufs[3] = {{(phases & 4) ? dQ : nullptr, (long long)B * H * n_q * d, k},
+                              {(phases & 2) ? dK : nullptr, (long long)B * H_kv * n_k * d, k},
+                              {(phases & 2) ? dV : nullptr, (long long)B * H_kv * n_k * dv, k}};
+    return debug_scan(bufs, 3, stream);
+  }
+  return ATTN_OK;
 }
 
 attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
@@ -167,6 +234,12 @@ attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, in
                            void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_common(phases, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b,
                     dropout, dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+static attn_status debug_topk(const int32_t* idx, const int32_t* length, int Tq, int topk, int Tkv, void* stream) {
+  int bad = 0;
+  if (debug_check_topk(idx, length, Tq, topk, Tkv, stream, &bad) != 0) return ATTN_ERR_HIP;
+  return bad ? ATTN_ERR_INVALID_ARG : ATTN_OK;
 }
 
 static attn_status check_sparse(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
@@ -205,8 +278,18 @@ attn_status attn_sparse_fwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H
   a.Q = Q; a.KV = KV; a.idx = topk_idx; a.length = topk_length; a.sink = attn_sink;
   a.O = O; a.LSE = LSE;
   a.lse_kv = kind == ATTN_LSE_KV;
+  const bool dbg = debug_enabled();
+  if (dbg) {
+    const attn_status cs = debug_topk(topk_idx, topk_length, Tq, topk, Tkv, stream);
+    if (cs != ATTN_OK) return cs;
+  }
   const int rc = launch_sparse_fwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
-  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+  if (rc != 0) return ATTN_ERR_HIP;
+  if (dbg) {
+    const DebugBuf bufs[2] = {{O, (long long)Tq * H * d_v, kind_of(dt)}, {LSE, (long long)Tq * H, 3}};
+    return debug_scan(bufs, 2, stream);
+  }
+  return ATTN_OK;
 }
 
 attn_status attn_sparse_fwd(attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v, int topk,
@@ -256,8 +339,19 @@ static attn_status sparse_bwd_common(int det, attn_lse_kind kind, attn_dtype dt,
   a.Dws = (float*)workspace;
   a.dsink_part = (float*)((char*)workspace + round_up((size_t)Tq * H * sizeof(float)));
   a.dKVws = (float*)((char*)workspace + 2 * round_up((size_t)Tq * H * sizeof(float)));
+  const bool dbg = debug_enabled();
+  if (dbg) {
+    const attn_status cs = debug_topk(topk_idx, topk_length, Tq, topk, Tkv, stream);
+    if (cs != ATTN_OK) return cs;
+  }
   const int rc = launch_sparse_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream);
-  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+  if (rc != 0) return ATTN_ERR_HIP;
+  if (dbg) {
+    const DebugBuf bufs[3] = {{dQ, (long long)Tq * H * d_qk, kind_of(dt)}, {dKV, (long long)Tkv * d_qk, kind_of(dt)},
+                              {dSink, dSink ? H : 0, 0}};
+    return debug_scan(bufs, 3, stream);
+  }
+  return ATTN_OK;
 }
 
 attn_status attn_sparse_bwd_lse(attn_lse_kind kind, attn_dtype dt, int Tq, int H, int Tkv, int d_qk, int d_v,

@@ -1,0 +1,389 @@
+// Dense masked attention backward, query-major dQ kernel (bf16/fp16 MFMA,
+// gfx950).  The operation and the split into three kernels are described in
+// dense_bwd.hip.
+#include "device.hpp"
+
+namespace ets {
+
+// --------------------------------------------------------------------- dQ
+// Query-major, the forward's layout: a workgroup owns 128 query rows (32 per
+// wave, queries along lanes) of one (batch, head) and streams the K/V tiles
+// of 64 keys through a two-stage LDS ring.  Per 32-key block mb a wave runs
+//   A(mb): S^T = K Q^T and dP^T = V G^T     (2 D/16 MFMAs)
+//   W(mb): gamma^T from S^T, dP^T, LSE, D    (VALU)
+//   B(mb): dQ^T += K^T gamma^T              (2 D/32 MFMAs)
+// in the fixed order A0 | A1+W0 | B0+W1 | B1, one MFMA per slot with
+// operands read two slots ahead; the next tile's copy is spread over A0.
+template <class E, int D, int MK, bool DROP>
+__global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a, int n_qtiles) {
+  constexpr int BK = 64;
+  constexpr int BQ = 128;
+  constexpr int KS = D / 16;
+  constexpr int MD = D / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BK * ROWB;
+  constexpr int NA = 2 * KS, NB = 2 * MD;  // slots of A(mb), B(mb)
+  constexpr int NSLOT = 2 * NA + 2 * NB;
+  typedef typename E::vec8 vec8;
+  typedef std::integral_constant<int, 0> Stage0;
+  typedef std::integral_constant<int, 1> Stage1;
+
+  __shared__ __attribute__((aligned(16))) char ldsK0[TILEB], ldsV0[TILEB], ldsK1[TILEB], ldsV1[TILEB];
+  auto kbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsK0;
+    else return (char ETS_LDS*)ldsK1;
+  };
+  auto vbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsV0;
+    else return (char ETS_LDS*)ldsV1;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int h32 = lane >> 5, l32 = lane & 31;
+  const int nq = a.nq, nk = a.nk;
+  const int BH = a.B * a.H;
+  const float sl2 = a.scale_log2;
+  const RowOps32<ROWB> rops(lane);
+  const TrOps32<ROWB> tops(lane);
+  const TileCopy<BK, D, 4> tcopy(wave, lane);
+  constexpr int PW = TileCopy<BK, D, 4>::PER_WAVE;
+  constexpr int NCOPY = 2 * PW;
+
+  // Persistent workgroups over (query tile, (batch, head)), heaviest query
+  // tiles first, in boustrophedon order.
+  const int G = (int)gridDim.x, n_items = n_qtiles * BH;
+  auto item_of = [&](int r) { return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  // key-tile range of query tile qt
+  // (active extents nqa x nka, row lower bounds >= smin; empty when hi < lo)
+  auto tile_range = [&](int qt, int nqa, int nka, int smin, int& lo, int& hi) __attribute__((always_inline)) {
+    const int q0 = qt * BQ, qlast = min(q0 + BQ, nqa) - 1;
+    lo = 0;
+    hi = (nka - 1) / BK;
+    if (nka < 1 || q0 >= nqa) hi = -1;
+    if (a.mask.causal) hi = min(hi, qlast / BK);
+    if (a.mask.window > 0) lo = max(0, (q0 - a.mask.window + 1) / BK);
+    if (smin > 0) lo = max(lo, smin / BK);
+  };
+  // The wave priority follows the key tiles the workgroup has left, so of two
+  // workgroups sharing a compute unit the one further behind issues first
+  // (with equal priorities the older one wins every tie).  rem is a scalar.
+  int rem = 0;
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = item_of(r);
+    if (item >= n_items) continue;
+    int lo, hi;
+    const int nqa = a.mask.lengths ? min(max(a.mask.lengths[(item % BH) / a.H], 0), nq) : nq;
+    tile_range(n_qtiles - 1 - item / BH, nqa, a.mask.lengths ? min(nqa, nk) : nk, 0, lo, hi);
+    rem += max(hi - lo + 1, 0);
+  }
+  auto set_prio = [&]() __attribute__((always_inline)) {
+    if (rem > 16) __builtin_amdgcn_s_setprio(3);
+    else if (rem > 8) __builtin_amdgcn_s_setprio(2);
+    else if (rem > 3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = item_of(r);
+    if (item >= n_items) continue;
+    const int qt = n_qtiles - 1 - item / BH;
+    const int bh = item % BH;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
+    const int q0 = qt * BQ, qw0 = q0 + wave * 32;
+    const int qi = qw0 + l32;  // this lane's query row
+
+    // active extents and row lower bounds of this batch (w: the wave's rows,
+    // g: the workgroup's)
+    const Layout lay = layout_of(a.mask, b, nq, nk);
+    const int nqa = lay.len, nka = lay.nka;
+    int sminw = (int)0x80000000, smaxw = (int)0x80000000, sming = sminw, smaxg = smaxw;
+    int st_i = (int)0x80000000;
+    if (lay.st) {
+      start_range(lay.st, qw0, qw0 + 31, nqa, lane, sminw, smaxw);
+      start_range(lay.st, q0, q0 + BQ - 1, nqa, lane, sming, smaxg);
+      if (qi < nqa) st_i = lay.st[qi];
+    }
+
+    const uint16_t* Qp = (const uint16_t*)a.Q + (size_t)bh * nq * D;
+    const uint16_t* Gp = (const uint16_t*)a.G + (size_t)bh * nq * D;
+    const uint16_t* Kp = (const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D;
+    const uint16_t* Vp = (const uint16_t*)a.V + (size_t)(b * a.Hkv + g) * nk * D;
+    const __amdgpu_buffer_rsrc_t Krs = make_rsrc(Kp, (uint32_t)nk * D * 2);
+    const __amdgpu_buffer_rsrc_t Vrs = make_rsrc(Vp, (uint32_t)nk * D * 2);
+
+    vec8 qreg[KS], greg[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 qv = u32x4{0, 0, 0, 0}, gv = u32x4{0, 0, 0, 0};
+      if (qi < nq) {
+        qv = *(const u32x4*)(Qp + (size_t)qi * D + 16 * kk + 8 * h32);
+        gv = *(const u32x4*)(Gp + (size_t)qi * D + 16 * kk + 8 * h32);
+      }
+      qreg[kk] = as_vec8<E>(qv);
+      greg[kk] = as_vec8<E>(gv);
+    }
+    const float lse2 = (qi < nq) ? a.Lws[(size_t)bh * nq + qi] : __builtin_huge_valf();
+    const float ndval = (qi < nq) ? a.Dws[(size_t)bh * nq + qi] : 0.f;  // -D
+    f32x16 dq[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) dq[md][r2] = 0.f;
+
+    int jt_lo, jt_hi;
+    tile_range(qt, nqa, nka, sming, jt_lo, jt_hi);
+    auto wg_nonempty = [&](int jt) {
+      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nqa, nka, sming, smaxg) != kEmpty;
+    };
+    auto next_of = [&](int jt) {
+      for (++jt; jt <= jt_hi; ++jt)
+        if (MK == kArith || wg_nonempty(jt)) return jt;
+      return -1;
+    };
+    auto copy_one = [&](int jt, auto st, int u) __attribute__((always_inline)) {
+      if (u < PW) tcopy.issue_one(kbuf(st), Krs, jt * BK, nk - 1, u);
+      else tcopy.issue_one(vbuf(st), Vrs, jt * BK, nk - 1, u - PW);
+    };
+    // operand t: A(mb) slots alternate K rows (S^T) and V rows (dP^T) per
+    // k-step; B(mb) slots read K^T for (16-key step kh, md)
+    auto operand = [&](auto st, int t) __attribute__((always_inline)) {
+      if (t < 2 * NA) {
+        const int mb = t / NA, u = t % NA, kk = u / 2;
+        return as_vec8<E>(lds_b128((u & 1) ? vbuf(st) : kbuf(st), rops.off(32 * mb, kk)));
+      }
+      const int u = t - 2 * NA, mb = u / NB, kh = (u % NB) / MD, md = u % MD;
+      return as_vec8<E>(tops.read(kbuf(st), 32 * mb + 16 * kh, md));
+    };
+    // key interval of this lane's row for arithmetic masks: key base + c is
+    // allowed iff (unsigned)(c - lo) <= rng
+    auto arith_interval = [&](int base, int& lo, unsigned& rng) __attribute__((always_inline)) {
+      int jlo = max(0, st_i), jhi = nka - 1;
+      if (a.mask.causal) jhi = min(jhi, qi);
+      if (a.mask.window > 0) jlo = max(jlo, qi - a.mask.window + 1);
+      const bool any = qi < nqa && jlo <= jhi;
+      lo = any ? jlo - base : (1 << 24);
+      rng = any ? (unsigned)(jhi - jlo) : 0u;
+    };
+    struct Gam {
+      uint32_t gw[8];
+      unsigned allow[4];
+      unsigned keep;  // dropout: bit 8 g4 + r keeps key key0 + 8 g4 + 4 h32 + r
+    };
+    // sub-part k = 2 g4 + half of W(mb): keys key0 + 8 g4 + 4 h32 + 2 half + e
+    auto weights = [&](Gam& w, const f32x16& sc, const f32x16& dp, int k, int key0, auto part_tag, bool cbm)
+                       __attribute__((always_inline)) {
+      constexpr bool PART = decltype(part_tag)::value;
+      const int g4 = k / 2, half = k % 2;
+      const int jj = key0 + 8 * g4 + 4 * h32;
+      if (half == 0) {
+        w.allow[g4] = 0xFu;
+        if constexpr (PART) {
+          if constexpr (MK == kArith) {
+            int lo;
+            unsigned rng;
+            arith_interval(jj, lo, rng);
+            unsigned al = 0;
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) al |= ((unsigned)(r2 - lo) <= rng ? 1u : 0u) << r2;
+            w.allow[g4] = al;
+          } else {
+            w.allow[g4] = allowed4<MK>(a.mask, qi, jj, nqa, nka, cbm, lay.st);
+          }
+        }
+      }
+      float gm[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r2 = 2 * half + e;
+        const float pv = fast_exp2(fmaf(sc[4 * g4 + r2], sl2, -lse2));
+        float dpv = dp[4 * g4 + r2];
+        if constexpr (DROP) dpv = ((w.keep >> (8 * g4 + r2)) & 1u) ? dpv * a.drop.inv_keep : 0.f;
+        const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
+        gm[e] = al ? pv * (dpv + ndval) : 0.f;
+      }
+      w.gw[2 * g4 + half] = E::pack2(gm[0], gm[1]);
+      materialize(w.gw[2 * g4 + half]);
+    };
+    auto pack_op = [&](const uint32_t (&x)[8], int kh) __attribute__((always_inline)) {
+      return as_vec8<E>(u32x4{x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]});
+    };
+
+    auto tile = [&](auto st, int jt, int jn, auto part_tag, bool cbm) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
+      const int j0 = jt * BK;
+      f32x16 sc[2], dp[2];
+      Gam w[2];
+      unsigned kd[4];  // dropout draws of the tile's four blocks of 8 keys per lane pair
+      vec8 opb[3];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) opb[k] = operand(st, k);
+      static_for<NSLOT>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (t + 2 < NSLOT) opb[(t + 2) % 3] = operand(st, t + 2);
+        const vec8 op = opb[t % 3];
+        if constexpr (t < 2 * NA) {
+          constexpr int mb = t / NA, u = t % NA, kk = u / 2;
+          if constexpr (u == 0) {
+#pragma unroll
+            for (int r2 = 0; r2 < 16; ++r2) { sc[mb][r2] = 0.f; dp[mb][r2] = 0.f; }
+          }
+          if constexpr (u & 1) dp[mb] = E::mfma32(op, greg[kk], dp[mb]);
+          else sc[mb] = E::mfma32(op, qreg[kk], sc[mb]);
+          if constexpr (mb == 0) {  // the copy of the next tile and the dropout keep bits
+            static_for<NCOPY>([&](auto uc) __attribute__((always_inline)) {
+              constexpr int cu = decltype(uc)::value;
+              if constexpr ((cu * NA) / NCOPY == u) copy_one(jn, Next{}, cu);
+            });
+            if constexpr (DROP) {
+              static_for<4>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr ((q * NA) / 4 == u) {
+                  kd[q] = keep_qm_draw(a.drop, bh, qi, j0 + 32 * (q / 2), h32, q % 2);
+                  if constexpr (q % 2 == 1) w[q / 2].keep = keep_qm_merge(kd[q - 1], kd[q], h32);
+                }
+              });
+            }
+          } else {  // W(0) under A(1)
+            static_for<8>([&](auto kc) __attribute__((always_inline)) {
+              constexpr int k = decltype(kc)::value;
+              if constexpr ((k * NA) / 8 == u) weights(w[0], sc[0], dp[0], k, j0, part_tag, cbm);
+            });
+          }
+        } else {
+          constexpr int u = t - 2 * NA, mb = u / NB, kh = (u % NB) / MD, md = u % MD;
+          dq[md] = E::mfma32(op, pack_op(w[mb].gw, kh), dq[md]);
+          if constexpr (mb == 0) {  // W(1) under B(0)
+            static_for<8>([&](auto kc) __attribute__((always_inline)) {
+              constexpr int k = decltype(kc)::value;
+              if constexpr ((k * NB) / 8 == u) weights(w[1], sc[1], dp[1], k, j0 + 32, part_tag, cbm);
+            });
+          }
+        }
+        ETS_FENCE();
+      });
+    };
+    auto empty_tile = [&](auto st, int jn) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, 1 - decltype(st)::value> Next;
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(jn, Next{}, u);
+    };
+    auto finish = [&]() __attribute__((always_inline)) {
+      wait_vm();
+      __syncthreads();
+    };
+    auto general_step = [&](auto st, int jt, int jn) __attribute__((always_inline)) {
+      set_prio();
+      --rem;
+      const int j0 = jt * BK;
+      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nqa, nka, sminw, smaxw);
+      const int cls = cinfo & kClassMask;
+      if (cls == kFull) tile(st, jt, jn, std::false_type{}, false);
+      else if (cls == kPartial) tile(st, jt, jn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      else empty_tile(st, jn);
+      finish();
+    };
+
+    int jt = -1;
+    if (jt_lo <= jt_hi) jt = (MK == kArith || wg_nonempty(jt_lo)) ? jt_lo : next_of(jt_lo);
+    if (jt >= 0) {
+#pragma unroll
+      for (int u = 0; u < NCOPY; ++u) copy_one(jt, Stage0{}, u);
+    }
+    finish();
+    // Tile number p runs on stage p % 2.  For arithmetic masks the tiles
+    // every row of the workgroup sees whole form one range; pairs of them
+    // starting on stage 0 run in a loop of their own (one code path, so the
+    // accumulators stay in place).
+    int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
+    if constexpr (MK == kArith) {
+      if (q0 + BQ <= nqa) {
+        int f_lo = jt_lo, f_hi = min(jt_hi, nka / BK - 1);
+        if (smaxg > 0) f_lo = max(f_lo, (smaxg + BK - 1) / BK);  // tiles at or past every row's lower bound
+        if (a.mask.causal) f_hi = min(f_hi, q0 >= BK - 1 ? (q0 - (BK - 1)) / BK : -1);
+        if (a.mask.window > 0) {
+          const int t = q0 + BQ - 1 - a.mask.window;  // full iff j0 > t
+          if (t >= 0) f_lo = max(f_lo, t / BK + 1);
+        }
+        if (f_lo <= f_hi) {
+          const int lo = f_lo - jt_lo, hi = f_hi - jt_lo + 1;
+          const int p0 = lo + (lo & 1), p1 = hi - ((hi - p0) & 1);
+          if (p0 < p1) { fp0 = p0; fp1 = p1; }
+        }
+      }
+    }
+    int p = 0;
+    auto general_run = [&](int p_end) __attribute__((always_inline)) {
+      for (; jt >= 0 && p < p_end; ++p) {
+        const int jn = next_of(jt);
+        if (p & 1) general_step(Stage1{}, jt, jn >= 0 ? jn : jt);
+        else general_step(Stage0{}, jt, jn >= 0 ? jn : jt);
+        jt = jn;
+      }
+    };
+    general_run(fp0);
+    if (fp0 < fp1) {
+      // general_run stopped at tile number fp0 < N: jt = jt_lo + p, and
+      // tile p + 1 is whole too
+      for (; p < fp1; p += 2) {
+        set_prio();
+        rem -= 2;
+        tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
+        finish();
+        const int jn = next_of(jt + 1);
+        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, std::false_type{}, false);
+        finish();
+        jt = jn;
+      }
+    }
+    general_run(1 << 30);
+
+    if (qi < nq) {
+      uint16_t* dQp = (uint16_t*)a.dQ + (size_t)bh * nq * D + (size_t)qi * D;
+      const float c = a.scale;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * md + 8 * g4 + 4 * h32;
+          u32x2 wv;
+          wv[0] = E::pack2(dq[md][4 * g4] * c, dq[md][4 * g4 + 1] * c);
+          wv[1] = E::pack2(dq[md][4 * g4 + 2] * c, dq[md][4 * g4 + 3] * c);
+          *(u32x2*)(dQp + col) = wv;
+        }
+    }
+  }
+}
+
+template <class E, int D, int MK, bool DROP>
+static int launch_dq_k(const DenseArgs& a, hipStream_t st) {
+  const int n_qtiles = (a.nq + 127) / 128;
+  const int n_items = n_qtiles * a.B * a.H;
+  int slots = 0;
+  ETS_TRY(resident_slots(dense_bwd_dq_kernel<E, D, MK, DROP>, 256, &slots));
+  ETS_TRY(launch((dense_bwd_dq_kernel<E, D, MK, DROP>), dim3(min(n_items, slots)), dim3(256), 0, st, a, n_qtiles));
+  return 0;
+}
+
+template <class E, int D>
+static int launch_dq(const DenseArgs& a, hipStream_t st) {
+  const int mk = mask_kind(a.mask);
+  if (a.drop.enabled) {
+    if (mk == kArith) return launch_dq_k<E, D, kArith, true>(a, st);
+    if (mk == kBlock) return launch_dq_k<E, D, kBlock, true>(a, st);
+    return launch_dq_k<E, D, kDenseM, true>(a, st);
+  }
+  if (mk == kArith) return launch_dq_k<E, D, kArith, false>(a, st);
+  if (mk == kBlock) return launch_dq_k<E, D, kBlock, false>(a, st);
+  return launch_dq_k<E, D, kDenseM, false>(a, st);
+}
+
+#if !defined(ETS_DT) || !defined(ETS_D)
+#error "compiled once per (dtype, head width): -DETS_DT=<1|2> -DETS_D=<64|128>"
+#endif
+template <>
+int launch_dense_dq_ed<ETS_DT, ETS_D>(const DenseArgs& a, void* stream) {
+  using E = std::conditional_t<ETS_DT == (int)Dt::BF16, BF16, F16>;
+  return launch_dq<E, ETS_D>(a, (hipStream_t)stream);
+}
+
+}  // namespace ets

@@ -28,6 +28,7 @@ __global__ __launch_bounds__(64) void f32_fwd_kernel(const DenseArgs a) {
   if (i >= a.nq) return;
   const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
   const int d = a.d, dv = a.dv, nk = a.nk;
+  const Layout lay = layout_of(a.mask, b, a.nq, nk);
   const float* Q = (const float*)a.Q + ((size_t)bh * a.nq + i) * d;
   const float* K = (const float*)a.K + (size_t)(b * a.Hkv + g) * nk * d;
   const float* V = (const float*)a.V + (size_t)(b * a.Hkv + g) * nk * dv;
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(64) void f32_fwd_kernel(const DenseArgs a) {
     float amax = kNegInf;
     bool any = false;
     for (int j = j0; j < j1; ++j) {
-      if (!allowed1<kDenseM>(a.mask, i, j, a.nq, nk, true)) continue;
+      if (!allowed1<kDenseM>(a.mask, i, j, lay.len, lay.nka, true, lay.st)) continue;
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < DM; ++r)
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(64) void f32_fwd_kernel(const DenseArgs a) {
 #pragma unroll
     for (int r = 0; r < DM; ++r) z[r] *= alpha;
     for (int j = j0; j < j1; ++j) {
-      if (!allowed1<kDenseM>(a.mask, i, j, a.nq, nk, true)) continue;
+      if (!allowed1<kDenseM>(a.mask, i, j, lay.len, lay.nka, true, lay.st)) continue;
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < DM; ++r)
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const DenseArgs a) {
   if (i >= a.nq) return;
   const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
   const int d = a.d, dv = a.dv, nk = a.nk;
+  const Layout lay = layout_of(a.mask, b, a.nq, nk);
   const size_t row = (size_t)bh * a.nq + i;
   const float* Q = (const float*)a.Q + row * d;
   const float* Gr = (const float*)a.G + row * dv;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const DenseArgs a) {
     dq[r] = 0.f;
   }
   for (int j = 0; j < nk; ++j) {
-    if (!allowed1<kDenseM>(a.mask, i, j, a.nq, nk, true)) continue;
+    if (!allowed1<kDenseM>(a.mask, i, j, lay.len, lay.nka, true, lay.st)) continue;
     float s = 0.f, dp = 0.f;
 #pragma unroll
     for (int r = 0; r < DM; ++r) {
@@ -136,6 +138,7 @@ __global__ __launch_bounds__(64) void f32_dkdv_kernel(const DenseArgs a) {
   if (j >= a.nk) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv, grp = a.H / a.Hkv;
   const int d = a.d, dv = a.dv, nq = a.nq;
+  const Layout lay = layout_of(a.mask, b, nq, a.nk);
   const float* Kr = (const float*)a.K + ((size_t)bg * a.nk + j) * d;
   const float* Vr = (const float*)a.V + ((size_t)bg * a.nk + j) * dv;
   float k[DM], v[DM], dk[DM], dvv[DM];
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(64) void f32_dkdv_kernel(const DenseArgs a) {
     const float* Q = (const float*)a.Q + (size_t)bh * nq * d;
     const float* G = (const float*)a.G + (size_t)bh * nq * dv;
     for (int i = 0; i < nq; ++i) {
-      if (!allowed1<kDenseM>(a.mask, i, j, nq, a.nk, true)) continue;
+      if (!allowed1<kDenseM>(a.mask, i, j, lay.len, lay.nka, true, lay.st)) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int r = 0; r < DM; ++r) {

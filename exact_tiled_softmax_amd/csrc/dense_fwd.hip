@@ -72,13 +72,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
   // triangle without atomics and keeps every slot busy until the end.
   const int G = (int)gridDim.x, n_items = n_qtiles * a.B * a.H;
   auto item_of = [&](int r) { return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x); };
-  // key-tile range of query tile qt
-  auto tile_range = [&](int qt, int& lo, int& hi) __attribute__((always_inline)) {
-    const int q0 = qt * BQ, qlast = min(q0 + BQ, a.nq) - 1;
+  // key-tile range of query tile qt for active extents nqa x nka and row
+  // lower bounds >= smin (an empty range when hi < lo)
+  auto tile_range = [&](int qt, int nqa, int nka, int smin, int& lo, int& hi) __attribute__((always_inline)) {
+    const int q0 = qt * BQ, qlast = min(q0 + BQ, nqa) - 1;
     lo = 0;
-    hi = (a.nk - 1) / BK;
+    hi = (nka - 1) / BK;
+    if (nka < 1 || q0 >= nqa) hi = -1;
     if (a.mask.causal) hi = min(hi, qlast / BK);
     if (a.mask.window > 0) lo = max(0, (q0 - a.mask.window + 1) / BK);
+    if (smin > 0) lo = max(lo, smin / BK);
   };
   // The wave priority follows the key tiles the workgroup has left, so of two
   // workgroups sharing a compute unit the one further behind issues first
@@ -89,7 +92,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     const int item = item_of(r);
     if (item >= n_items) continue;
     int lo, hi;
-    tile_range(n_qtiles - 1 - item / (a.B * a.H), lo, hi);
+    const int nqa = a.mask.lengths ? min(max(a.mask.lengths[(item % (a.B * a.H)) / a.H], 0), a.nq) : a.nq;
+    tile_range(n_qtiles - 1 - item / (a.B * a.H), nqa, a.mask.lengths ? min(nqa, a.nk) : a.nk, 0, lo, hi);
     rem += max(hi - lo + 1, 0);
   }
   auto set_prio = [&]() __attribute__((always_inline)) {
@@ -110,6 +114,17 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     const int nq = a.nq, nk = a.nk;
     const int q0 = qt * BQ, qw0 = q0 + wave * 32;
     const int qi = qw0 + l32;  // this lane's query row
+    // active extents and row lower bounds of this batch; smin/smax bound the
+    // lower bounds of the wave's (w) and the workgroup's (g) active rows
+    const Layout lay = layout_of(a.mask, b, nq, nk);
+    const int nqa = lay.len, nka = lay.nka;
+    int sminw = (int)0x80000000, smaxw = (int)0x80000000, sming = sminw, smaxg = smaxw;
+    int st_i = (int)0x80000000;  // lower bound of this lane's row
+    if (lay.st) {
+      start_range(lay.st, qw0, qw0 + 31, nqa, lane, sminw, smaxw);
+      start_range(lay.st, q0, q0 + BQ - 1, nqa, lane, sming, smaxg);
+      if (qi < nqa) st_i = lay.st[qi];
+    }
 
     const uint16_t* Qp = (const uint16_t*)a.Q + (size_t)bh * nq * D;
     const uint16_t* Kp = (const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D;
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
 
     // key-tile range of the workgroup
     int jt_lo, jt_hi;
-    tile_range(qt, jt_lo, jt_hi);
+    tile_range(qt, nqa, nka, sming, jt_lo, jt_hi);
 
     const TileCopy<BK, D, NW> tcopy(wave, lane);
     constexpr int NCOPY = 2 * TileCopy<BK, D, NW>::PER_WAVE;  // copy instructions per wave per tile
@@ -176,11 +191,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     // allowed keys of this lane's row form one interval for arithmetic masks:
     // key0 + c allowed iff lo <= c <= lo + rng (unsigned compare of c - lo)
     auto arith_interval = [&](int key0, int& lo, unsigned& rng) __attribute__((always_inline)) {
-      int jlo = 0, jhi = nk - 1;
+      int jlo = max(0, st_i), jhi = nka - 1;
       if (a.mask.causal) jhi = min(jhi, qi);
       if (a.mask.window > 0) jlo = max(jlo, qi - a.mask.window + 1);
       const int base = key0 + 4 * h32;
-      const bool any = qi < nq && jlo <= jhi;
+      const bool any = qi < nqa && jlo <= jhi;
       lo = any ? jlo - base : (1 << 24);
       rng = any ? (unsigned)(jhi - jlo) : 0u;
     };
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       } else {
   #pragma unroll
         for (int g4 = r0 / 4; g4 < r0 / 4 + 2; ++g4) {
-          const unsigned allow = allowed4<MK>(a.mask, qi, key0 + 8 * g4 + 4 * h32, nq, nk, cbm);
+          const unsigned allow = allowed4<MK>(a.mask, qi, key0 + 8 * g4 + 4 * h32, nqa, nka, cbm, lay.st);
   #pragma unroll
           for (int r = 0; r < 4; ++r) s[4 * g4 + r] = ((allow >> r) & 1u) ? s[4 * g4 + r] * sl2 : kNegInf;
         }
@@ -340,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     // jt_lo .. jt_hi, and those every row of the workgroup sees whole form one
     // range; pairs of them starting on stage 0 take the fixed-order path.
     auto wg_nonempty = [&](int jt) {
-      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nq, nk) != kEmpty;
+      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nqa, nka, sming, smaxg) != kEmpty;
     };
     auto next_of = [&](int jt) {
       if constexpr (MK == kArith) {
@@ -356,8 +371,9 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
 
     int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
     if constexpr (MK == kArith) {
-      if (q0 + BQ <= nq) {
-        int f_lo = jt_lo, f_hi = min(jt_hi, nk / BK - 1);
+      if (q0 + BQ <= nqa) {
+        int f_lo = jt_lo, f_hi = min(jt_hi, nka / BK - 1);
+        if (smaxg > 0) f_lo = max(f_lo, (smaxg + BK - 1) / BK);  // tiles at or past every row's lower bound
         if (a.mask.causal) f_hi = min(f_hi, q0 >= BK - 1 ? (q0 - (BK - 1)) / BK : -1);
         if (a.mask.window > 0) {
           const int t = q0 + BQ - 1 - a.mask.window;  // full iff j0 > t
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       set_prio();
       --rem;
       const int j0 = jt * BK;
-      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nq, nk);
+      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nqa, nka, sminw, smaxw);
       const int cls = cinfo & kClassMask;
       if (cls == kFull) tile(st, jt, jn, std::false_type{}, false);
       else if (cls == kPartial) tile(st, jt, jn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
@@ -469,15 +485,13 @@ static int launch_fwd_t(const DenseArgs& a, void* stream) {
   }
 }
 
-bool dense_mfma_supported(int d, int dv) { return d == dv && (d == 64 || d == 128); }
-
-int launch_dense_fwd(const DenseArgs& a, Dt dt, void* stream) {
-  if (dt == Dt::BF16) {
-    if (a.d == 128) return launch_fwd_t<BF16, 128, 4>(a, stream);
-    return launch_fwd_t<BF16, 64, 4>(a, stream);
-  }
-  if (a.d == 128) return launch_fwd_t<F16, 128, 4>(a, stream);
-  return launch_fwd_t<F16, 64, 4>(a, stream);
+#if !defined(ETS_DT) || !defined(ETS_D)
+#error "dense_fwd.hip is compiled once per (dtype, head width): -DETS_DT=<1|2> -DETS_D=<64|128>"
+#endif
+template <>
+int launch_dense_fwd_ed<ETS_DT, ETS_D>(const DenseArgs& a, void* stream) {
+  using E = std::conditional_t<ETS_DT == (int)Dt::BF16, BF16, F16>;
+  return launch_fwd_t<E, ETS_D, 4>(a, stream);
 }
 
 }  // namespace ets

@@ -24,6 +24,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define ETS_LDS __attribute__((address_space(3)))
 
@@ -464,49 +465,106 @@ enum MaskKind { kArith = 0, kBlock = 1, kDenseM = 2 };
 
 inline int mask_kind(const MaskArgs& m) { return m.dense_mask ? kDenseM : (m.block_mask ? kBlock : kArith); }
 
-// Single (row i, key j) test.  check_bm = false skips the block-mask lookup
-// (the caller has established that the block mask allows the whole tile).
+// Per-batch view of the layout parts of the allowed set (variable lengths and
+// packed segments): rows and keys at or past `len` are inactive, and key j is
+// allowed for row i only if j >= st[i] (st null: no lower bound).  `nka` is the
+// key extent the allowed set can reach (len when lengths are given, else nk).
+struct Layout {
+  int len, nka;
+  const int32_t* st;
+};
+__device__ __forceinline__ Layout layout_of(const MaskArgs& m, int b, int nq, int nk) {
+  Layout l;
+  l.len = nq;
+  l.nka = nk;
+  l.st = nullptr;
+  if (m.lengths) {
+    l.len = min(max(m.lengths[b], 0), nq);
+    l.nka = min(l.len, nk);
+  }
+  if (m.starts) l.st = m.starts + (size_t)b * nq;
+  return l;
+}
+
+// Single (row i, key j) test; nq / nk are the active extents and st the row
+// lower bounds of the batch (or null).  check_bm = false skips the block-mask
+// lookup (the caller has established that the block mask allows the whole
+// tile).
 template <int MK>
-__device__ __forceinline__ bool allowed1(const MaskArgs& m, int i, int j, int nq, int nk, bool check_bm) {
+__device__ __forceinline__ bool allowed1(const MaskArgs& m, int i, int j, int nq, int nk, bool check_bm,
+                                         const int32_t* st = nullptr) {
   if (i >= nq || j >= nk) return false;
   if (m.causal && j > i) return false;
   if (m.window > 0 && i - j >= m.window) return false;
+  if (st && j < st[i]) return false;
   if constexpr (MK >= kBlock)
     if (check_bm && m.block_mask && m.block_mask[(size_t)(i / m.bq) * m.nbk + j / m.bk] == 0) return false;
   if constexpr (MK == kDenseM)
-    if (m.dense_mask && m.dense_mask[(size_t)i * nk + j] == 0) return false;
+    if (m.dense_mask && m.dense_mask[(size_t)i * m.dm_stride + j] == 0) return false;
   return true;
 }
 
 // Allowed bits of keys j0 .. j0+3 for query row i (bit r <-> key j0 + r).
 template <int MK>
-__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk, bool check_bm) {
+__device__ __forceinline__ unsigned allowed4(const MaskArgs& m, int i, int j0, int nq, int nk, bool check_bm,
+                                             const int32_t* st = nullptr) {
   unsigned bits = 0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) bits |= (allowed1<MK>(m, i, j0 + r, nq, nk, check_bm) ? 1u : 0u) << r;
+  for (int r = 0; r < 4; ++r) bits |= (allowed1<MK>(m, i, j0 + r, nq, nk, check_bm, st) ? 1u : 0u) << r;
   return bits;
 }
 
 // Allowed bits of query rows i0 .. i0+3 for key j (bit r <-> row i0 + r).
 template <int MK>
-__device__ __forceinline__ unsigned allowed4_rows(const MaskArgs& m, int i0, int j, int nq, int nk, bool check_bm) {
+__device__ __forceinline__ unsigned allowed4_rows(const MaskArgs& m, int i0, int j, int nq, int nk, bool check_bm,
+                                                  const int32_t* st = nullptr) {
   unsigned bits = 0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) bits |= (allowed1<MK>(m, i0 + r, j, nq, nk, check_bm) ? 1u : 0u) << r;
+  for (int r = 0; r < 4; ++r) bits |= (allowed1<MK>(m, i0 + r, j, nq, nk, check_bm, st) ? 1u : 0u) << r;
   return bits;
+}
+
+// Lowest and highest row lower bound (starts) over rows [r0, r1] (inclusive)
+// that are active (< len): every lane of the wave computes the same pair.
+// Rows past len do not count; with none active, smin = INT_MAX (every key is
+// below it) and smax = INT_MIN.  Covers up to 128 rows.
+__device__ __forceinline__ void start_range(const int32_t* st, int r0, int r1, int len, int lane, int& smin,
+                                            int& smax) {
+  r1 = min(r1, len - 1);
+  int lo = 0x7fffffff, hi = (int)0x80000000;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = r0 + lane + 64 * k;
+    if (r <= r1) {
+      const int v = st[r];
+      lo = min(lo, v);
+      hi = max(hi, v);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off, 64));
+    hi = max(hi, __shfl_xor(hi, off, 64));
+  }
+  smin = lo;
+  smax = hi;
 }
 
 enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2, kClassMask = 3, kCheckBlockMask = 4 };
 
 // Classify the rectangle of query rows [ia, ib] x keys [ja, jb] (inclusive;
 // jb may run past nk for a ragged last tile).  Uniform across the wave.
+// nq / nk are the active extents; smin / smax bound the row lower bounds
+// (starts) of the rectangle's active rows (INT_MIN, INT_MIN without starts).
 // Returns kEmpty, kFull or kPartial, plus kCheckBlockMask when the block mask
 // is mixed inside the rectangle and must be read per element.
 template <int MK>
-__device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int ja, int jb, int nq, int nk) {
+__device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int ja, int jb, int nq, int nk,
+                                        int smin = (int)0x80000000, int smax = (int)0x80000000) {
   if (ia >= nq || ja >= nk) return kEmpty;
+  if (jb < smin) return kEmpty;
   // rows or keys past the end are present in the tile: mask them per element
-  int cls = (jb >= nk || ib >= nq) ? kPartial : kFull;
+  int cls = (jb >= nk || ib >= nq || ja < smax) ? kPartial : kFull;
   if (ib >= nq) ib = nq - 1;
   if (jb >= nk) jb = nk - 1;
   if (m.causal) {

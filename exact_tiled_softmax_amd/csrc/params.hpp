@@ -16,6 +16,9 @@ struct MaskArgs {
   int bq, bk;                 // block_mask granularity
   int nbk;                    // ceil(nk / bk): row length of block_mask
   const uint8_t* dense_mask;  // [nq][nk] or null
+  int dm_stride;              // nk: row length of dense_mask
+  const int32_t* lengths;     // [B] active rows (and keys) per batch, or null
+  const int32_t* starts;      // [B][nq] lowest allowed key per row, or null
 };
 
 // Inverted dropout: keep iff the key's 16-bit Philox draw >= threshold.
@@ -61,6 +64,23 @@ struct SparseArgs {
 // Kernel launchers (defined in the .hip files).  Each returns 0 on success or
 // a hipError_t value.  They assume validated arguments.
 int launch_dense_fwd(const DenseArgs& a, Dt dt, void* stream);
+
+// The MFMA kernels of one (dtype, head width): dense_fwd.hip, dense_dkdv.hip
+// and dense_dq.hip are each compiled once per combination (-DETS_DT, -DETS_D),
+// so that the instantiations build in parallel; each object defines its
+// specialisations.  DT is (int)Dt.
+template <int DT, int D> int launch_dense_fwd_ed(const DenseArgs& a, void* stream);
+template <int DT, int D> int launch_dense_dkdv_ed(const DenseArgs& a, void* stream);
+template <int DT, int D> int launch_dense_dq_ed(const DenseArgs& a, void* stream);
+#define ETS_DECLARE_ED(DT, D)                                                 \
+  template <> int launch_dense_fwd_ed<DT, D>(const DenseArgs& a, void* stream);  \
+  template <> int launch_dense_dkdv_ed<DT, D>(const DenseArgs& a, void* stream); \
+  template <> int launch_dense_dq_ed<DT, D>(const DenseArgs& a, void* stream);
+ETS_DECLARE_ED(1, 64)
+ETS_DECLARE_ED(1, 128)
+ETS_DECLARE_ED(2, 64)
+ETS_DECLARE_ED(2, 128)
+#undef ETS_DECLARE_ED
 // phases: bit 0 = D prepass, bit 1 = dK/dV, bit 2 = dQ
 int launch_dense_bwd(const DenseArgs& a, Dt dt, void* stream, int phases);
 int launch_dense_fwd_f32(const DenseArgs& a, void* stream);
@@ -69,6 +89,17 @@ int launch_sparse_fwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_sparse_bwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_dropout_mask(const DropArgs& d, int B, int H, int nq, int nk, uint8_t* xi, void* stream);
 int launch_mfma_probe(int waves_per_simd, int iters, float* sink, int sink_len, long long* mfmas, void* stream);
+
+// Debug checks (debug.hip).  Each returns 0 or a hipError_t value and sets
+// *bad (host) when the check fails; each synchronises the stream.
+struct DebugBuf {
+  const void* ptr;
+  long long count;  // elements
+  int kind;         // 0 fp32, 1 fp16, 2 bf16, 3 fp32 with -inf allowed
+};
+int debug_check_lengths(const int32_t* lengths, int B, int n, void* stream, int* bad);
+int debug_check_topk(const int32_t* idx, const int32_t* length, int Tq, int topk, int Tkv, void* stream, int* bad);
+int debug_scan_nonfinite(const DebugBuf* bufs, int nbufs, void* stream, int* bad);
 
 // Shapes the MFMA kernels are built for.
 bool dense_mfma_supported(int d, int dv);

@@ -55,17 +55,25 @@ constexpr double kFixInv = 1.0 / 4294967296.0;
 
 bool sparse_supported(int H, int dqk, int dv) { return H == sp::H && dqk == sp::DQK && dv == sp::DV; }
 
+// Valid selection count of token t: topk_length[t] clamped to [0, topk]
+// (topk without lengths).
+__device__ __forceinline__ int sel_count(const SparseArgs& a, int t) {
+  return a.length ? min(max(a.length[t], 0), a.topk) : a.topk;
+}
+
 // Gather of one tile of selected rows (global -> registers -> LDS).  The row
 // indices of a tile are read one tile before its rows (load_idx, then fetch a
-// tile later), so a fetch never waits on an index load.
+// tile later), so a fetch never waits on an index load.  A slot past L or an
+// index outside [0, Tkv) reads as a zero row: no access leaves the KV tensor.
 struct Gather {
   u32x4 pre[sp::NCH];
-  int jrow[sp::NCH];  // KV row of each chunk of the next tile to fetch (-1: padding slot)
-  __device__ __forceinline__ void load_idx(const int32_t* idx_t, int L, int u0, int tid) {
+  int jrow[sp::NCH];  // KV row of each chunk of the next tile to fetch (-1: zero row)
+  __device__ __forceinline__ void load_idx(const int32_t* idx_t, int L, int Tkv, int u0, int tid) {
 #pragma unroll
     for (int v = 0; v < sp::NCH; ++v) {
       const int slot = u0 + (tid + 256 * v) / sp::CPR;
-      jrow[v] = slot < L ? idx_t[slot] : -1;
+      const int j = slot < L ? idx_t[slot] : -1;
+      jrow[v] = (unsigned)j < (unsigned)Tkv ? j : -1;
     }
   }
   __device__ __forceinline__ void fetch(const uint16_t* KV, int tid) {
@@ -84,19 +92,19 @@ struct Gather {
     }
   }
   // prologue: tile 0 into buf, the indices of tile 1 loaded
-  __device__ __forceinline__ void start(const uint16_t* KV, const int32_t* idx_t, int L, int ntiles,
+  __device__ __forceinline__ void start(const uint16_t* KV, const int32_t* idx_t, int L, int Tkv, int ntiles,
                                         char ETS_LDS* buf, int tid) {
-    load_idx(idx_t, L, 0, tid);
+    load_idx(idx_t, L, Tkv, 0, tid);
     fetch(KV, tid);
     stash(buf, tid);
-    if (ntiles > 1) load_idx(idx_t, L, sp::BK, tid);
+    if (ntiles > 1) load_idx(idx_t, L, Tkv, sp::BK, tid);
   }
   // at the start of tile it: rows of tile it + 1 requested, indices of tile it + 2 loaded
-  __device__ __forceinline__ void next(const uint16_t* KV, const int32_t* idx_t, int L, int it, int ntiles,
-                                       int tid) {
+  __device__ __forceinline__ void next(const uint16_t* KV, const int32_t* idx_t, int L, int Tkv, int it,
+                                       int ntiles, int tid) {
     if (it + 1 < ntiles) {
       fetch(KV, tid);
-      if (it + 2 < ntiles) load_idx(idx_t, L, (it + 2) * sp::BK, tid);
+      if (it + 2 < ntiles) load_idx(idx_t, L, Tkv, (it + 2) * sp::BK, tid);
     }
   }
 };
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
   const int head = 16 * wave + l16;
   const uint16_t* KV = (const uint16_t*)a.KV;
   const int32_t* idx_t = a.idx + (size_t)t * a.topk;
-  const int L = a.length ? a.length[t] : a.topk;
+  const int L = sel_count(a, t);
 
   vec8 qreg[KSQ];
   const uint16_t* Qh = (const uint16_t*)a.Q + ((size_t)t * H + head) * DQK;
@@ -168,12 +176,12 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(const SparseArgs a) 
   const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
-    gat.start(KV, idx_t, L, ntiles, smem, tid);
+    gat.start(KV, idx_t, L, a.Tkv, ntiles, smem, tid);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int u0 = it * BK;
-    gat.next(KV, idx_t, L, it, ntiles, tid);
+    gat.next(KV, idx_t, L, a.Tkv, it, ntiles, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
 
     f32x4 s[2];
@@ -339,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
   const int head = 16 * wave + l16;
   const uint16_t* KV = (const uint16_t*)a.KV;
   const int32_t* idx_t = a.idx + (size_t)t * a.topk;
-  const int L = a.length ? a.length[t] : a.topk;
+  const int L = sel_count(a, t);
   const size_t th = (size_t)t * H + head;
 
   vec8 qreg[KSQ], greg[KSV];
@@ -364,12 +372,12 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dq_kernel(const SparseArgs 
   const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
-    gat.start(KV, idx_t, L, ntiles, smem, tid);
+    gat.start(KV, idx_t, L, a.Tkv, ntiles, smem, tid);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int u0 = it * BK;
-    gat.next(KV, idx_t, L, it, ntiles, tid);
+    gat.next(KV, idx_t, L, a.Tkv, it, ntiles, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
     vec8 pb, db;
     recompute_p_ds<E>(kt, qreg, greg, rops, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
   const int head = 16 * wave + l16;
   const uint16_t* KV = (const uint16_t*)a.KV;
   const int32_t* idx_t = a.idx + (size_t)t * a.topk;
-  const int L = a.length ? a.length[t] : a.topk;
+  const int L = sel_count(a, t);
   const size_t th = (size_t)t * H + head;
   const int c0w = wave * (DQK / 4);       // first output column of this wave
 
@@ -471,14 +479,14 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
   const TrOps16<ROWB> tops(lane);
   const int ntiles = (L + BK - 1) / BK;
   if (ntiles > 0) {
-    gat.start(KV, idx_t, L, ntiles, smem, tid);
+    gat.start(KV, idx_t, L, a.Tkv, ntiles, smem, tid);
   }
   __syncthreads();
   float* ws = a.dKVws;
   const float al = a.scale;
   for (int it = 0; it < ntiles; ++it) {
     const int u0 = it * BK;
-    gat.next(KV, idx_t, L, it, ntiles, tid);
+    gat.next(KV, idx_t, L, a.Tkv, it, ntiles, tid);
     const char ETS_LDS* kt = smem + (it & 1) * TILEB;
     vec8 pb, db;
     recompute_p_ds<E>(kt, qreg, greg, rops, lane, u0, L, a.scale_log2, lse2, Dv, pb, db);
@@ -511,10 +519,10 @@ __global__ __launch_bounds__(256, 1) void sparse_bwd_dkv_kernel(const SparseArgs
       int jrow[4];
       bool valid[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r) {  // rows outside [0, Tkv) get no update
         const int slot = u0 + 16 * nb + 4 * G + r;
-        valid[r] = slot < L;
-        jrow[r] = valid[r] ? idx_t[slot] : 0;
+        jrow[r] = slot < L ? idx_t[slot] : -1;
+        valid[r] = (unsigned)jrow[r] < (unsigned)a.Tkv;
       }
 #pragma unroll
       for (int m = 0; m < MW; ++m) {

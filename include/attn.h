@@ -14,7 +14,23 @@
  *     accumulated into.
  *   - `stream` is a hipStream_t (NULL = the default stream).
  *   - A failed kernel launch returns ATTN_ERR_HIP.
- *   - Non-finite input values are not checked; they propagate.
+ *   - Non-finite input values are not checked on the normal path; they
+ *     propagate.
+ *   - Debug checks: when the environment variable ATTN_DEBUG holds a nonzero
+ *     integer at the time of a call, the call also (a) validates on the device,
+ *     before any attention kernel is launched, the values of index and length
+ *     arrays the host cannot see (dense `lengths` in [0, n]; sparse
+ *     `topk_length` in [0, topk] and every `topk_idx` entry below it in
+ *     [0, Tkv)), returning ATTN_ERR_INVALID_ARG with no output written; and (b)
+ *     after the kernels, scans every output for NaN or infinity (-inf is
+ *     allowed in an LSE, where it marks an empty row) and returns
+ *     ATTN_ERR_NONFINITE if it finds one.  The course this library follows
+ *     refuses non-finite results; device writes cannot be rolled back, so the
+ *     outputs' contents are unspecified after ATTN_ERR_NONFINITE.  Debug
+ *     checks synchronise the stream and never trap.
+ *   - Size limits (ATTN_ERR_UNSUPPORTED beyond them): every per-(batch, head)
+ *     tensor below 2^32 bytes; B * H * n_q and B * H_kv * n_k at most
+ *     2^28 - 64 rows; fp32 path: B * H at most 65535.
  *
  * Sources.  The operation is defined on these pages:
  *   [P1] alphabetamath.cc, "Tiled attention and its recomputed reverse pass
@@ -42,7 +58,8 @@ typedef enum {
   ATTN_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment, scale, rate or mask */
   ATTN_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size() */
-  ATTN_ERR_HIP = 4          /* a HIP launch failed */
+  ATTN_ERR_HIP = 4,         /* a HIP launch failed */
+  ATTN_ERR_NONFINITE = 5    /* debug checks only: an output holds NaN or infinity */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
@@ -58,6 +75,21 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype;
  *               only if block_mask[i/block_q][j/block_k] != 0; NULL: off
  *   dense_mask  device pointer to uint8 [n_q][n_k], shared by all batches and
  *               heads; NULL: off
+ *   lengths     device pointer to int32 [B] (requires n_q == n_k): the active
+ *               length of each batch's sequence; rows i >= lengths[b] are
+ *               inactive (Y = 0, LSE = -inf, zero gradients) and keys
+ *               j >= lengths[b] are never allowed.  Values outside [0, n] are
+ *               clamped into it (rejected by the debug checks).  NULL: off
+ *   starts      device pointer to int32 [B][n_q]: key j is allowed for row i
+ *               of batch b only if j >= starts[b][i], the row's lower key
+ *               bound; for packed segments (several sequences concatenated
+ *               along n) starts[b][i] is the first row of the segment that
+ *               holds row i, which with `causal` gives block-diagonal causal
+ *               attention.  Any int32 value is valid.  NULL: off
+ * lengths and starts are the variable-length layout of [P3] ("Rescale earlier
+ * mass before adding a new tile": the per-row lower bound and inactive padded
+ * rows; "Change attention evaluation inside the existing model": active
+ * lengths and packed-segment boundaries intersected with the causal range).
  * A NULL attn_mask_t* means every key is allowed.  A row whose allowed set is
  * empty gets Y = 0 and LSE = -inf and contributes nothing to any gradient
  * (the convention [P3] uses for query rows without keys).
@@ -68,6 +100,8 @@ typedef struct {
   const uint8_t* block_mask;
   int32_t block_q, block_k;
   const uint8_t* dense_mask;
+  const int32_t* lengths;
+  const int32_t* starts;
 } attn_mask_t;
 
 /*
@@ -176,8 +210,13 @@ attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, in
  *   dt           ATTN_BF16 or ATTN_F16
  *   Q            [Tq][H][d_qk];  KV [Tkv][d_qk] (the value is its first d_v columns)
  *   topk_idx     int32 [Tq][topk]; entries < L_t must lie in [0, Tkv), the
- *                rest are never read; duplicates are allowed
- *   topk_length  int32 [Tq], values in [0, topk], or NULL
+ *                rest are never read; duplicates are allowed.  An entry
+ *                outside [0, Tkv) is not checked on the normal path: it
+ *                reads as an all-zero row (score 0, value 0), no memory
+ *                outside KV is touched and the backward drops its dKV
+ *                contribution (the debug checks reject it)
+ *   topk_length  int32 [Tq], values in [0, topk] (clamped into it; rejected by
+ *                the debug checks), or NULL
  *   attn_sink    fp32 [H] or NULL
  *   O            [Tq][H][d_v] output;  LSE fp32 [Tq][H] output
  * Shapes: H == 64, d_qk == 576, d_v == 512.  A token with no selected row

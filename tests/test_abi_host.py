@@ -155,3 +155,48 @@ def test_one_hip_runtime_per_process():
             "print(len(m))\n")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, check=True).stdout
     assert out.strip().splitlines()[-1] == "1"
+
+
+@pytest.mark.parametrize("case", [
+    # per-(batch, head) tensors must stay below 2^32 bytes (32-bit buffer extents)
+    dict(n_q=1 << 24, n_k=1 << 24, d=128, dv=128, code=2),
+    dict(n_k=1 << 24, d=128, dv=128, code=2),
+    # at most 2^28 - 64 rows (32-bit workspace offsets)
+    dict(B=2, H=1 << 8, H_kv=1 << 8, n_q=1 << 19, n_k=64, code=2),
+    # fp32 path: B * H at most 65535
+    dict(dt=0, B=256, H=256, H_kv=256, d=16, dv=16, code=2),
+    # lengths need n_q == n_k and 4-byte aligned layout arrays
+    dict(mask={"lengths": P}, n_k=100, code=1),
+    dict(mask={"lengths": P + 2}, code=1),
+    dict(mask={"starts": P + 1}, code=1),
+])
+def test_fwd_limits_and_layout_checks(case):
+    import exact_tiled_softmax_amd as ets
+    a = dict(dt=ets.ATTN_BF16, B=1, H=2, H_kv=2, n_q=64, n_k=64, d=64, dv=64, mask=None)
+    a.update({k: v for k, v in case.items() if k != "code"})
+    st = ets.attn_fwd(a["dt"], a["B"], a["H"], a["H_kv"], a["n_q"], a["n_k"], a["d"], a["dv"], P, P, P,
+                      a["mask"], 0.125, 0, None, P, P, stream=0, raise_on_error=False)
+    assert st == case["code"], case
+    if case["code"] == 2:  # the backward applies the same limits
+        st = ets.attn_bwd(a["dt"], a["B"], a["H"], a["H_kv"], a["n_q"], a["n_k"], a["d"], a["dv"], P, P, P, P, P, P,
+                          a["mask"], 0.125, 0, None, P, P, P, P, 1 << 62, stream=0, raise_on_error=False)
+        assert st == 2
+
+
+def test_nonfinite_status_has_a_name():
+    import exact_tiled_softmax_amd as ets
+    assert ets.ATTN_ERR_NONFINITE == 5
+    assert "non-finite" in ets.attn_status_string(ets.ATTN_ERR_NONFINITE)
+
+
+def test_mask_struct_layout_matches_the_header():
+    # attn_mask_t: int32 causal, int32 window, pointer, int32 block_q, int32
+    # block_k, pointer, then the lengths and starts pointers
+    import ctypes
+    import exact_tiled_softmax_amd as ets
+    names = [f[0] for f in ets.Mask._fields_]
+    assert names == ["causal", "window", "block_mask", "block_q", "block_k", "dense_mask", "lengths", "starts"]
+    assert ctypes.sizeof(ets.Mask) == 48
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {\n  int32_t causal;"):text.index("} attn_mask_t;")]
+    assert body.index("lengths") < body.index("starts") and "const int32_t* lengths;" in body

@@ -175,3 +175,15 @@ def sparse_arrays(w, seed=None):
     out["idx"] = idx
     out["length"] = length
     return out
+
+
+def packed_starts(segments, n):
+    """starts [n] for packed segments: row i's lower key bound is the first row
+    of the segment holding it.  ``segments`` lists segment lengths that sum to
+    at most n; rows past them form one last segment."""
+    starts = np.zeros(n, dtype=np.int32)
+    o = 0
+    for s in list(segments) + [max(0, n - int(np.sum(segments)))]:
+        starts[o:o + s] = o
+        o += s
+    return starts
