@@ -18,7 +18,7 @@ __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
     "ATTN_ERR_NONFINITE",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
-    "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
+    "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_fwd_lse", "attn_sparse_bwd_lse", "attn_sparse_bwd_det", "attn_sparse_bwd_det_workspace_size",
     "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_status_string", "library_path", "lib",
 ]
@@ -87,6 +87,8 @@ lib.attn_bwd_workspace_size.restype = _sz
 lib.attn_bwd_workspace_size.argtypes = [_i] * 8
 lib.attn_bwd.restype = _i
 lib.attn_bwd.argtypes = ([_i] + [_i] * 7 + [_vp] * 6 + [_pm, _f, _i, _pd] + [_vp] * 3 + [_vp, _sz, _vp])
+lib.attn_bwd_noalloc.restype = _i
+lib.attn_bwd_noalloc.argtypes = lib.attn_bwd.argtypes[:-3] + [_vp]
 lib.attn_bwd_phase.restype = _i
 lib.attn_bwd_phase.argtypes = [_i] + lib.attn_bwd.argtypes
 lib.attn_sparse_fwd.restype = _i
@@ -182,6 +184,14 @@ def attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, b
                       _ptr(G), _mask(mask), float(scale), int(block_b), _drop(dropout), _ptr(dQ),
                       _ptr(dK), _ptr(dV), _ptr(workspace), int(workspace_bytes), _stream(stream))
     return _check(st, "attn_bwd", raise_on_error)
+
+
+def attn_bwd_noalloc(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout,
+                     dQ, dK, dV, stream=None, raise_on_error=True):
+    st = lib.attn_bwd_noalloc(dt, B, H, H_kv, n_q, n_k, d, dv, _ptr(Q), _ptr(K), _ptr(V), _ptr(Y), _ptr(LSE),
+                              _ptr(G), _mask(mask), float(scale), int(block_b), _drop(dropout), _ptr(dQ),
+                              _ptr(dK), _ptr(dV), _stream(stream))
+    return _check(st, "attn_bwd_noalloc", raise_on_error)
 
 
 def attn_bwd_phase(phases, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b,

@@ -2,10 +2,13 @@
 // Every check happens before any launch; on failure nothing is launched and
 // no output is written.  The declarations and their contracts are in
 // include/attn.h.
+#include <hip/hip_runtime.h>
+
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "params.hpp"
@@ -225,6 +228,46 @@ attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, in
                      void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_common(7, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout,
                     dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+// Fixed device scratch of attn_bwd_noalloc: the backward workspace (D_i and
+// the base-2 LSE of every query row) for callers that cannot allocate.  Each
+// GPU holds its own copy until the process ends.  Host code never passes this
+// name to a kernel or a copy: it uses the address hipGetSymbolAddress returns
+// for the current device (noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+static attn_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[256] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_HIP;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_noalloc(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                             const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
+                             const void* G, const attn_mask_t* mask, float scale, int block_b,
+                             const attn_dropout_t* dropout, void* dQ, void* dK, void* dV, void* stream) {
+  // the argument checks first, so that a bad call touches no device state
+  attn_status st = check_dense(dt, B, H, H_kv, n_q, n_k, d, dv, mask, scale, block_b, dropout);
+  if (st != ATTN_OK) return st;
+  if (attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv) > kNoAllocScratchBytes) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != ATTN_OK) return st;
+  return bwd_common(7, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout, dQ, dK,
+                    dV, ws, kNoAllocScratchBytes, stream);
 }
 
 attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,

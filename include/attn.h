@@ -198,6 +198,24 @@ attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, in
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as attn_bwd, without the
+ * workspace arguments: the workspace is a fixed 16 MiB device array inside the
+ * library (each GPU holds its own copy until the process ends).  Nothing is
+ * allocated or freed.  Limit: attn_bwd_workspace_size() of the call at most
+ * 16 MiB, i.e. B * H * n_q <= 2,097,088 query rows; beyond it the call returns
+ * ATTN_ERR_WORKSPACE and launches nothing.  Every call on one GPU uses that
+ * GPU's array: calls ordered on one stream are safe (each writes the array
+ * before reading it), but calls that overlap in time on one GPU (other streams
+ * or threads) race and give wrong gradients.
+ */
+attn_status attn_bwd_noalloc(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                             const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
+                             const void* G, const attn_mask_t* mask, float scale, int block_b,
+                             const attn_dropout_t* dropout, void* dQ, void* dK, void* dV, void* stream);
+
+/*
  * attn_sparse_fwd -- shared-KV top-k sparse attention with sink ([P5]
  * sections 1, 2 and 7.1).  For token t and head h, with the selected rows
  * I = topk_idx[t][0 : L_t] (L_t = topk_length[t], or topk when NULL):
