@@ -37,10 +37,12 @@ import workloads  # noqa: E402
 
 KERNEL_SOURCES = {
     "fwd": ["exact_tiled_softmax_amd/csrc/dense_fwd.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
-    "bwd_dkdv": ["exact_tiled_softmax_amd/csrc/dense_bwd.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
-    "bwd_dq": ["exact_tiled_softmax_amd/csrc/dense_bwd.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+    "bwd_dkdv": ["exact_tiled_softmax_amd/csrc/dense_dkdv.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+    "bwd_dq": ["exact_tiled_softmax_amd/csrc/dense_dq.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
     "sparse_fwd": ["exact_tiled_softmax_amd/csrc/sparse.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
+    "sparse_dkv": ["exact_tiled_softmax_amd/csrc/sparse.hip", "exact_tiled_softmax_amd/csrc/device.hpp"],
 }
+RIDGE = 2500.0e12 / 8000.0e9  # flop per byte where the bf16 MFMA and HBM roofs meet
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA peaks (fp32: vector)
 PEAK_HBM_GBS = 8000.0
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
@@ -49,6 +51,40 @@ METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak (causal, seq 2048, d=12
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def host_cores_and_model():
+    """(threads the oracle's BLAS uses, CPU model name from /proc/cpuinfo)."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return int(cores), model
+
+
+def dense_algorithmic_bytes(w):
+    """Compulsory HBM bytes per launch of each dense kernel: every input read
+    once, every output written once (dtype-sized tensors, fp32 LSE / D rows)."""
+    esz = 4 if w.dtype == "f32" else 2
+    q = w.B * w.H * w.n * w.d * esz            # Q, dQ
+    g = w.B * w.H * w.n * w.dv * esz           # G, Y
+    k = w.B * w.H_kv * w.n * w.d * esz         # K, dK
+    v = w.B * w.H_kv * w.n * w.dv * esz        # V, dV
+    row = w.B * w.H * w.n * 4                  # one fp32 per query row (LSE, D, LSE2)
+    return {"fwd": q + k + v + g + row,        # Q, K, V read; Y, LSE written
+            "bwd_prep": 2 * g + row + 2 * row,  # G, Y, LSE read; D, LSE2 written
+            "bwd_dkdv": q + g + k + v + 2 * row + k + v,  # Q, G, K, V, LSE2, D read; dK, dV written
+            "bwd_dq": q + g + k + v + 2 * row + q}         # Q, G, K, V, LSE2, D read; dQ written
 
 
 def sources_sha256(kernel):
@@ -134,11 +170,7 @@ def cpu_baseline_dense(w, arr, block_mask, budget_s=12.0):
     """The fp64 oracle, untouched, timed on the host on a bounded sample of
     (batch, head) lanes of the same workload."""
     from oracle import dense
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    cores, model = host_cores_and_model()
     allowed = dense.Allowed(w.n, w.n, causal=w.causal, window=w.window, block_mask=block_mask,
                             block_q=w.mask_tile, block_k=w.mask_tile)
     drop = dense.Dropout(float(np.float32(w.rho)), seed=w.drop_seed) if w.rho > 0 else None
@@ -157,7 +189,7 @@ def cpu_baseline_dense(w, arr, block_mask, budget_s=12.0):
         if t_total >= budget_s:
             break
     tflops = lanes * pairs_lane * per_pair / t_total / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "cpu_model": model, "kind": "oracle",
             "sample": f"fp64 forward + VJP of {lanes} of {w.B * w.H} (batch, head) lanes "
                       f"({lanes * pairs_lane} allowed pairs) in {t_total:.1f} s"}
 
@@ -165,7 +197,7 @@ def cpu_baseline_dense(w, arr, block_mask, budget_s=12.0):
 def bench_dense(w, args):
     import torch
     import exact_tiled_softmax_amd as ets
-    from tests import gpu_helpers as gh
+    from workloads import device as gh
 
     if args.no_dropout and w.rho > 0:
         import dataclasses
@@ -218,19 +250,27 @@ def bench_dense(w, args):
     f_fwd, f_bwd = flops["fwd"], flops["bwd_dkdv"] + flops["bwd_dq"]
     peak = PEAK_TFLOPS[w.dtype]
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    prep_bytes = 2 * w.B * w.H * w.n * w.dv * (2 if w.dtype != "f32" else 4) + 4 * w.B * w.H * w.n
+    nbytes = dense_algorithmic_bytes(w)
     kernels = {}
     for n in names:
-        if n == "bwd_prep":
-            gbs = prep_bytes / (kern_ms[n] * 1e-3) / 1e9
-            kernels[n] = {"ms": kern_ms[n], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
-        else:
+        gbs = nbytes[n] / (kern_ms[n] * 1e-3) / 1e9
+        kernels[n] = {"ms": kern_ms[n], "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                      "algorithmic_bytes": nbytes[n]}
+        if n != "bwd_prep":
             tf = flops[n] / (kern_ms[n] * 1e-3) / 1e12
-            kernels[n] = {"ms": kern_ms[n], "TFLOP/s": tf, "frac_peak": tf / peak}
+            kernels[n].update({"TFLOP/s": tf, "frac_peak": tf / peak})
     dom = max(["fwd", "bwd_dkdv", "bwd_dq"], key=lambda n: kern_ms[n])
-    roofline = {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": peak, "unit": "TFLOP/s",
-                "frac": kernels[dom]["TFLOP/s"] / peak, "traffic": recorded_traffic(dom, w.name), "kernel": dom,
-                "flops_per_launch": flops[dom]}
+    # the roof that binds: MFMA when the step's flops per compulsory byte
+    # exceed the ridge point, else HBM
+    intensity = (f_fwd + f_bwd) / sum(nbytes.values())
+    if intensity >= RIDGE or w.dtype == "f32":
+        roofline = {"bound": "mfma", "achieved": kernels[dom]["TFLOP/s"], "peak": peak, "unit": "TFLOP/s",
+                    "frac": kernels[dom]["TFLOP/s"] / peak, "flops_per_launch": flops[dom]}
+    else:
+        roofline = {"bound": "hbm", "achieved": kernels[dom]["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": kernels[dom]["GB/s"] / PEAK_HBM_GBS, "bytes_per_launch": nbytes[dom]}
+    roofline.update({"traffic": recorded_traffic(dom, w.name), "kernel": dom, "flop_per_byte": intensity,
+                     "ridge_flop_per_byte": RIDGE})
     fwd_tf = f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
     bwd_ms = kern_ms["bwd_prep"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
     bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
@@ -256,11 +296,7 @@ def bench_dense(w, args):
 def cpu_baseline_sparse(w, a, budget_s=12.0):
     """The fp64 oracle timed on a bounded sample of tokens of the sparse workload."""
     from oracle import sparse
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    cores, model = host_cores_and_model()
     sink = a["sink"].astype(np.float64)
     per_pair = w.H * ((2 * w.dqk + 2 * w.dv) + (6 * w.dqk + 4 * w.dv))
     toks, pairs, t_total = [], 0, 0.0
@@ -273,14 +309,15 @@ def cpu_baseline_sparse(w, a, budget_s=12.0):
         pairs += int(a["length"][t])
         if t_total >= budget_s:
             break
-    return {"value": pairs * per_pair / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": pairs * per_pair / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu_model": model,
+            "kind": "oracle",
             "sample": f"fp64 forward + VJP of {len(toks)} of {w.Tq} tokens ({pairs} valid slots) in {t_total:.1f} s"}
 
 
 def bench_sparse(w, args):
     import torch
     import exact_tiled_softmax_amd as ets
-    from tests import gpu_helpers as gh
+    from workloads import device as gh
 
     a = workloads.sparse_arrays(w)
     dt = DTYPE_CODE[w.dtype]

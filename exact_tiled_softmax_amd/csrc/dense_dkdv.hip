@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     const int k0 = kb * 128, kw0 = k0 + 32 * wave;
     const int key = kw0 + l32;  // this lane's key
     // active extents and row lower bounds of this batch
-    const Layout lay = layout_of(a.mask, b, nq, nk);
+    const Layout lay = layout_of<MK>(a.mask, b, nq, nk);
     const int nqa = lay.len, nka = lay.nka;
 
     const uint16_t* Kp = (const uint16_t*)a.K + (size_t)bg * nk * D;
@@ -195,15 +195,37 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     if (a.mask.window > 0) qt_hi = min(qt_hi, (klast + a.mask.window - 1) / BQ);
     const int n_qt = qt_hi - qt_lo + 1;
     const int total = (n_qt > 0) ? n_qt * grp : 0;
-    auto wg_nonempty = [&](int st) {
-      const int qt = qt_lo + st % n_qt;
-      return classify<MK>(a.mask, qt * BQ, qt * BQ + BQ - 1, k0, k0 + 127, nqa, nka) != kEmpty;
+    // step classes of the per-element mask kinds, 64 steps at a time (row
+    // lower bounds vary per step: with them a step is never taken as full
+    // here, and the per-element test applies them)
+    TileClasses tc;
+    tc.base = -1;
+    auto classes_for = [&](int s0) __attribute__((always_inline)) {
+      if (tc.covers(s0)) return;
+      const int s = s0 + lane;
+      int cg = kEmpty, cw = kEmpty;
+      if (s < total) {
+        const int qb = (qt_lo + s % n_qt) * BQ;
+        cg = classify<MK>(a.mask, qb, qb + BQ - 1, k0, k0 + 127, nqa, nka);
+        cw = classify<MK>(a.mask, qb, qb + BQ - 1, kw0, kw0 + 31, nqa, nka);
+        if (lay.st && (cw & kClassMask) == kFull) cw = kPartial;
+      }
+      tc.set(s0, cg, cw);
     };
-    auto next_of = [&](int st) {
-      for (++st; st < total; ++st)
-        if (MK == kArith || wg_nonempty(st)) return st;
-      return -1;
+    auto first_from = [&](int s) {  // first step >= s the workgroup's keys see, or -1
+      if constexpr (is_interval(MK)) {
+        return s < total ? s : -1;
+      } else {
+        while (s < total) {
+          classes_for(s);
+          const int f = tc.next_nonempty(s);
+          if (f >= 0) return f < total ? f : -1;
+          s = tc.base + 64;
+        }
+        return -1;
+      }
     };
+    auto next_of = [&](int st) { return first_from(st + 1); };
     auto step_rows = [&](int st, size_t& lane_off, int& qb0) __attribute__((always_inline)) {
       const int h = g * grp + st / n_qt;
       lane_off = (size_t)(b * a.H + h) * nq;
@@ -292,13 +314,13 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
     // sub-part k = 2 g4 + half: rows r2 = 2 half, 2 half + 1 of group g4
     auto weights = [&](Weights& w, const f32x16& sc, const f32x16& dp, int k, int mq, int qb0, int lane_bh,
                        auto part_tag, bool cbm, const char ETS_LDS* lb) __attribute__((always_inline)) {
-      constexpr bool PART = decltype(part_tag)::value;
+      constexpr bool PART = decltype(part_tag)::value != kWhole;
       const int g4 = k / 2, half = k % 2;
       const int qr = 32 * mq + 8 * g4 + 4 * h32;
       if (half == 0) {
         w.allow[g4] = 0xFu;
         if constexpr (PART) {
-          if constexpr (MK == kArith) {
+          if constexpr (decltype(part_tag)::value == kPartIv) {
             int lo;
             unsigned rng;
             arith_interval(qb0 + qr, lo, rng);
@@ -428,18 +450,34 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
       size_t lo;
       int qb0;
       step_rows(st, lo, qb0);
-      int smin = (int)0x80000000, smax = (int)0x80000000;
-      if (lay.st) step_start_range(stg, qb0, smin, smax);
-      const int cinfo = classify<MK>(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nqa, nka, smin, smax);
+      int cinfo;
+      if constexpr (is_interval(MK)) {
+        int smin = (int)0x80000000, smax = (int)0x80000000;
+        if (lay.st) step_start_range(stg, qb0, smin, smax);
+        cinfo = classify<MK>(a.mask, qb0, qb0 + BQ - 1, kw0, kw0 + 31, nqa, nka, smin, smax);
+      } else {
+        classes_for(st);
+        cinfo = tc.wave_class(st);
+      }
       const int cls = cinfo & kClassMask;
-      if (cls == kFull) step(stg, st, sn, std::false_type{}, false);
-      else if (cls == kPartial) step(stg, st, sn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      if (cls == kFull) {
+        step(stg, st, sn, BodyTag<kWhole>{}, false);
+      } else if (cls == kPartial) {
+        // a tile mask that is uniform over the wave's rectangle leaves only the interval parts
+        if constexpr (MK == kDenseM) step(stg, st, sn, BodyTag<kPartEl>{}, (cinfo & kCheckBlockMask) != 0);
+        else if constexpr (MK == kBlock) {
+          if (cinfo & kCheckBlockMask) step(stg, st, sn, BodyTag<kPartEl>{}, true);
+          else step(stg, st, sn, BodyTag<kPartIv>{}, false);
+        } else {
+          step(stg, st, sn, BodyTag<kPartIv>{}, false);
+        }
+      }
       else empty_step(stg, sn);
       finish();
     };
 
     int st = -1;
-    if (total > 0) st = (MK == kArith || wg_nonempty(0)) ? 0 : next_of(0);
+    if (total > 0) st = first_from(0);
     if (st >= 0) {
       copy_lse(st, Stage0{});
 #pragma unroll
@@ -460,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         ++p;
       }
     };
-    if constexpr (MK == kArith) {
+    if constexpr (is_interval(MK)) {
       // local q-tile indices i (qb0 = (qt_lo + i) BQ) whose rows see all 128 keys
       // (row lower bounds are not known per step here: none with starts)
       int i_lo = 0, i_hi = n_qt - 1;
@@ -481,10 +519,10 @@ __global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs 
         }
         if ((a1 - a0) & 1) --a1;
         for (; st < a1; st += 2, p += 2) {
-          step(Stage0{}, st, st + 1, std::false_type{}, false);
+          step(Stage0{}, st, st + 1, BodyTag<kWhole>{}, false);
           finish();
           const int sn = next_of(st + 1);
-          step(Stage1{}, st + 1, sn >= 0 ? sn : st + 1, std::false_type{}, false);
+          step(Stage1{}, st + 1, sn >= 0 ? sn : st + 1, BodyTag<kWhole>{}, false);
           finish();
         }
         if (st >= total) st = -1;
@@ -531,10 +569,12 @@ static int launch_dkdv(const DenseArgs& a, hipStream_t st) {
   const int mk = mask_kind(a.mask);
   if (a.drop.enabled) {
     if (mk == kArith) return launch_dkdv_k<E, D, kArith, true>(a, st);
+    if (mk == kLayout) return launch_dkdv_k<E, D, kLayout, true>(a, st);
     if (mk == kBlock) return launch_dkdv_k<E, D, kBlock, true>(a, st);
     return launch_dkdv_k<E, D, kDenseM, true>(a, st);
   }
   if (mk == kArith) return launch_dkdv_k<E, D, kArith, false>(a, st);
+  if (mk == kLayout) return launch_dkdv_k<E, D, kLayout, false>(a, st);
   if (mk == kBlock) return launch_dkdv_k<E, D, kBlock, false>(a, st);
   return launch_dkdv_k<E, D, kDenseM, false>(a, st);
 }

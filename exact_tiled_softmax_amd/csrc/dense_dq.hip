@@ -73,8 +73,8 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
     const int item = item_of(r);
     if (item >= n_items) continue;
     int lo, hi;
-    const int nqa = a.mask.lengths ? min(max(a.mask.lengths[(item % BH) / a.H], 0), nq) : nq;
-    tile_range(n_qtiles - 1 - item / BH, nqa, a.mask.lengths ? min(nqa, nk) : nk, 0, lo, hi);
+    const int nqa = (MK != kArith && a.mask.lengths) ? min(max(a.mask.lengths[(item % BH) / a.H], 0), nq) : nq;
+    tile_range(n_qtiles - 1 - item / BH, nqa, (MK != kArith && a.mask.lengths) ? min(nqa, nk) : nk, 0, lo, hi);
     rem += max(hi - lo + 1, 0);
   }
   auto set_prio = [&]() __attribute__((always_inline)) {
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
 
     // active extents and row lower bounds of this batch (w: the wave's rows,
     // g: the workgroup's)
-    const Layout lay = layout_of(a.mask, b, nq, nk);
+    const Layout lay = layout_of<MK>(a.mask, b, nq, nk);
     const int nqa = lay.len, nka = lay.nka;
     int sminw = (int)0x80000000, smaxw = (int)0x80000000, sming = sminw, smaxg = smaxw;
     int st_i = (int)0x80000000;
@@ -132,14 +132,33 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
 
     int jt_lo, jt_hi;
     tile_range(qt, nqa, nka, sming, jt_lo, jt_hi);
-    auto wg_nonempty = [&](int jt) {
-      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nqa, nka, sming, smaxg) != kEmpty;
+    // tile classes of the per-element mask kinds, 64 tiles at a time
+    TileClasses tc;
+    tc.base = -1;
+    auto classes_for = [&](int t0) __attribute__((always_inline)) {
+      if (tc.covers(t0)) return;
+      const int t = t0 + lane;
+      int cg = kEmpty, cw = kEmpty;
+      if (t <= jt_hi) {
+        cg = classify<MK>(a.mask, q0, q0 + BQ - 1, t * BK, t * BK + BK - 1, nqa, nka, sming, smaxg);
+        cw = classify<MK>(a.mask, qw0, qw0 + 31, t * BK, t * BK + BK - 1, nqa, nka, sminw, smaxw);
+      }
+      tc.set(t0, cg, cw);
     };
-    auto next_of = [&](int jt) {
-      for (++jt; jt <= jt_hi; ++jt)
-        if (MK == kArith || wg_nonempty(jt)) return jt;
-      return -1;
+    auto first_from = [&](int t) {  // first tile >= t the workgroup sees, or -1
+      if constexpr (is_interval(MK)) {
+        return t <= jt_hi ? t : -1;
+      } else {
+        while (t <= jt_hi) {
+          classes_for(t);
+          const int f = tc.next_nonempty(t);
+          if (f >= 0) return f <= jt_hi ? f : -1;
+          t = tc.base + 64;
+        }
+        return -1;
+      }
     };
+    auto next_of = [&](int jt) { return first_from(jt + 1); };
     auto copy_one = [&](int jt, auto st, int u) __attribute__((always_inline)) {
       if (u < PW) tcopy.issue_one(kbuf(st), Krs, jt * BK, nk - 1, u);
       else tcopy.issue_one(vbuf(st), Vrs, jt * BK, nk - 1, u - PW);
@@ -172,13 +191,13 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
     // sub-part k = 2 g4 + half of W(mb): keys key0 + 8 g4 + 4 h32 + 2 half + e
     auto weights = [&](Gam& w, const f32x16& sc, const f32x16& dp, int k, int key0, auto part_tag, bool cbm)
                        __attribute__((always_inline)) {
-      constexpr bool PART = decltype(part_tag)::value;
+      constexpr bool PART = decltype(part_tag)::value != kWhole;
       const int g4 = k / 2, half = k % 2;
       const int jj = key0 + 8 * g4 + 4 * h32;
       if (half == 0) {
         w.allow[g4] = 0xFu;
         if constexpr (PART) {
-          if constexpr (MK == kArith) {
+          if constexpr (decltype(part_tag)::value == kPartIv) {
             int lo;
             unsigned rng;
             arith_interval(jj, lo, rng);
@@ -275,16 +294,32 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       set_prio();
       --rem;
       const int j0 = jt * BK;
-      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nqa, nka, sminw, smaxw);
+      int cinfo;
+      if constexpr (is_interval(MK)) {
+        cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nqa, nka, sminw, smaxw);
+      } else {
+        classes_for(jt);
+        cinfo = tc.wave_class(jt);
+      }
       const int cls = cinfo & kClassMask;
-      if (cls == kFull) tile(st, jt, jn, std::false_type{}, false);
-      else if (cls == kPartial) tile(st, jt, jn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      if (cls == kFull) {
+        tile(st, jt, jn, BodyTag<kWhole>{}, false);
+      } else if (cls == kPartial) {
+        // a tile mask that is uniform over the wave's tile leaves only the interval parts
+        if constexpr (MK == kDenseM) tile(st, jt, jn, BodyTag<kPartEl>{}, (cinfo & kCheckBlockMask) != 0);
+        else if constexpr (MK == kBlock) {
+          if (cinfo & kCheckBlockMask) tile(st, jt, jn, BodyTag<kPartEl>{}, true);
+          else tile(st, jt, jn, BodyTag<kPartIv>{}, false);
+        } else {
+          tile(st, jt, jn, BodyTag<kPartIv>{}, false);
+        }
+      }
       else empty_tile(st, jn);
       finish();
     };
 
     int jt = -1;
-    if (jt_lo <= jt_hi) jt = (MK == kArith || wg_nonempty(jt_lo)) ? jt_lo : next_of(jt_lo);
+    if (jt_lo <= jt_hi) jt = first_from(jt_lo);
     if (jt >= 0) {
 #pragma unroll
       for (int u = 0; u < NCOPY; ++u) copy_one(jt, Stage0{}, u);
@@ -295,7 +330,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
     // starting on stage 0 run in a loop of their own (one code path, so the
     // accumulators stay in place).
     int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
-    if constexpr (MK == kArith) {
+    if constexpr (is_interval(MK)) {
       if (q0 + BQ <= nqa) {
         int f_lo = jt_lo, f_hi = min(jt_hi, nka / BK - 1);
         if (smaxg > 0) f_lo = max(f_lo, (smaxg + BK - 1) / BK);  // tiles at or past every row's lower bound
@@ -327,10 +362,10 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       for (; p < fp1; p += 2) {
         set_prio();
         rem -= 2;
-        tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
+        tile(Stage0{}, jt, jt + 1, BodyTag<kWhole>{}, false);
         finish();
         const int jn = next_of(jt + 1);
-        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, std::false_type{}, false);
+        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, BodyTag<kWhole>{}, false);
         finish();
         jt = jn;
       }
@@ -369,10 +404,12 @@ static int launch_dq(const DenseArgs& a, hipStream_t st) {
   const int mk = mask_kind(a.mask);
   if (a.drop.enabled) {
     if (mk == kArith) return launch_dq_k<E, D, kArith, true>(a, st);
+    if (mk == kLayout) return launch_dq_k<E, D, kLayout, true>(a, st);
     if (mk == kBlock) return launch_dq_k<E, D, kBlock, true>(a, st);
     return launch_dq_k<E, D, kDenseM, true>(a, st);
   }
   if (mk == kArith) return launch_dq_k<E, D, kArith, false>(a, st);
+  if (mk == kLayout) return launch_dq_k<E, D, kLayout, false>(a, st);
   if (mk == kBlock) return launch_dq_k<E, D, kBlock, false>(a, st);
   return launch_dq_k<E, D, kDenseM, false>(a, st);
 }

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(64) void f32_fwd_kernel(const DenseArgs a) {
   if (i >= a.nq) return;
   const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
   const int d = a.d, dv = a.dv, nk = a.nk;
-  const Layout lay = layout_of(a.mask, b, a.nq, nk);
+  const Layout lay = layout_of<kDenseM>(a.mask, b, a.nq, nk);
   const float* Q = (const float*)a.Q + ((size_t)bh * a.nq + i) * d;
   const float* K = (const float*)a.K + (size_t)(b * a.Hkv + g) * nk * d;
   const float* V = (const float*)a.V + (size_t)(b * a.Hkv + g) * nk * dv;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const DenseArgs a) {
   if (i >= a.nq) return;
   const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
   const int d = a.d, dv = a.dv, nk = a.nk;
-  const Layout lay = layout_of(a.mask, b, a.nq, nk);
+  const Layout lay = layout_of<kDenseM>(a.mask, b, a.nq, nk);
   const size_t row = (size_t)bh * a.nq + i;
   const float* Q = (const float*)a.Q + row * d;
   const float* Gr = (const float*)a.G + row * dv;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64) void f32_dkdv_kernel(const DenseArgs a) {
   if (j >= a.nk) return;
   const int b = bg / a.Hkv, g = bg % a.Hkv, grp = a.H / a.Hkv;
   const int d = a.d, dv = a.dv, nq = a.nq;
-  const Layout lay = layout_of(a.mask, b, nq, a.nk);
+  const Layout lay = layout_of<kDenseM>(a.mask, b, nq, a.nk);
   const float* Kr = (const float*)a.K + ((size_t)bg * a.nk + j) * d;
   const float* Vr = (const float*)a.V + ((size_t)bg * a.nk + j) * dv;
   float k[DM], v[DM], dk[DM], dvv[DM];

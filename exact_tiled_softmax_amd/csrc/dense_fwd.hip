@@ -92,8 +92,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     const int item = item_of(r);
     if (item >= n_items) continue;
     int lo, hi;
-    const int nqa = a.mask.lengths ? min(max(a.mask.lengths[(item % (a.B * a.H)) / a.H], 0), a.nq) : a.nq;
-    tile_range(n_qtiles - 1 - item / (a.B * a.H), nqa, a.mask.lengths ? min(nqa, a.nk) : a.nk, 0, lo, hi);
+    const int nqa = (MK != kArith && a.mask.lengths) ? min(max(a.mask.lengths[(item % (a.B * a.H)) / a.H], 0), a.nq) : a.nq;
+    tile_range(n_qtiles - 1 - item / (a.B * a.H), nqa, (MK != kArith && a.mask.lengths) ? min(nqa, a.nk) : a.nk, 0, lo, hi);
     rem += max(hi - lo + 1, 0);
   }
   auto set_prio = [&]() __attribute__((always_inline)) {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     const int qi = qw0 + l32;  // this lane's query row
     // active extents and row lower bounds of this batch; smin/smax bound the
     // lower bounds of the wave's (w) and the workgroup's (g) active rows
-    const Layout lay = layout_of(a.mask, b, nq, nk);
+    const Layout lay = layout_of<MK>(a.mask, b, nq, nk);
     const int nqa = lay.len, nka = lay.nka;
     int sminw = (int)0x80000000, smaxw = (int)0x80000000, sming = sminw, smaxg = smaxw;
     int st_i = (int)0x80000000;  // lower bound of this lane's row
@@ -199,8 +199,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       lo = any ? jlo - base : (1 << 24);
       rng = any ? (unsigned)(jhi - jlo) : 0u;
     };
-    auto mask_scale = [&](f32x16& s, int r0, int key0, bool cbm) __attribute__((always_inline)) {
-      if constexpr (MK == kArith) {
+    auto mask_scale = [&](f32x16& s, int r0, int key0, bool cbm, auto body) __attribute__((always_inline)) {
+      if constexpr (decltype(body)::value == kPartIv) {
         int lo;
         unsigned rng;
         arith_interval(key0, lo, rng);
@@ -221,14 +221,14 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     auto summary_part = [&](Summary& st, f32x16& s, auto part_c, auto part_tag, int key0, bool cbm)
                             __attribute__((always_inline)) {
       constexpr int part = decltype(part_c)::value;
-      constexpr bool PART = decltype(part_tag)::value;
+      constexpr bool PART = decltype(part_tag)::value != kWhole;
       if constexpr (part == 0) {
-        if constexpr (PART) mask_scale(s, 0, key0, cbm);
+        if constexpr (PART) mask_scale(s, 0, key0, cbm, part_tag);
         st.mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   #pragma unroll
         for (int r = 4; r < 8; ++r) st.mx = fmaxf(st.mx, s[r]);
       } else if constexpr (part == 1) {
-        if constexpr (PART) mask_scale(s, 8, key0, cbm);
+        if constexpr (PART) mask_scale(s, 8, key0, cbm, part_tag);
   #pragma unroll
         for (int r = 8; r < 16; ++r) st.mx = fmaxf(st.mx, s[r]);
       } else if constexpr (part == 2) {
@@ -354,23 +354,38 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
     // keeps the issue free of branches).  For arithmetic masks the tiles are
     // jt_lo .. jt_hi, and those every row of the workgroup sees whole form one
     // range; pairs of them starting on stage 0 take the fixed-order path.
-    auto wg_nonempty = [&](int jt) {
-      return classify<MK>(a.mask, q0, q0 + BQ - 1, jt * BK, jt * BK + BK - 1, nqa, nka, sming, smaxg) != kEmpty;
+    // tile classes of the per-element mask kinds, 64 tiles at a time
+    TileClasses tc;
+    tc.base = -1;
+    auto classes_for = [&](int t0) __attribute__((always_inline)) {
+      if (tc.covers(t0)) return;
+      const int t = t0 + lane;
+      int cg = kEmpty, cw = kEmpty;
+      if (t <= jt_hi) {
+        cg = classify<MK>(a.mask, q0, q0 + BQ - 1, t * BK, t * BK + BK - 1, nqa, nka, sming, smaxg);
+        cw = classify<MK>(a.mask, qw0, qw0 + 31, t * BK, t * BK + BK - 1, nqa, nka, sminw, smaxw);
+      }
+      tc.set(t0, cg, cw);
     };
-    auto next_of = [&](int jt) {
-      if constexpr (MK == kArith) {
-        return jt < jt_hi ? jt + 1 : -1;
+    auto first_from = [&](int t) {  // first tile >= t the workgroup sees, or -1
+      if constexpr (is_interval(MK)) {
+        return t <= jt_hi ? t : -1;
       } else {
-        for (++jt; jt <= jt_hi; ++jt)
-          if (wg_nonempty(jt)) return jt;
+        while (t <= jt_hi) {
+          classes_for(t);
+          const int f = tc.next_nonempty(t);
+          if (f >= 0) return f <= jt_hi ? f : -1;
+          t = tc.base + 64;
+        }
         return -1;
       }
     };
+    auto next_of = [&](int jt) { return first_from(jt + 1); };
     int jt = -1;
-    if (jt_lo <= jt_hi) jt = (MK == kArith || wg_nonempty(jt_lo)) ? jt_lo : next_of(jt_lo);
+    if (jt_lo <= jt_hi) jt = first_from(jt_lo);
 
     int fp0 = 1 << 30, fp1 = 1 << 30;  // fixed-order pairs cover tile numbers [fp0, fp1) when fp0 < fp1
-    if constexpr (MK == kArith) {
+    if constexpr (is_interval(MK)) {
       if (q0 + BQ <= nqa) {
         int f_lo = jt_lo, f_hi = min(jt_hi, nka / BK - 1);
         if (smaxg > 0) f_lo = max(f_lo, (smaxg + BK - 1) / BK);  // tiles at or past every row's lower bound
@@ -403,10 +418,26 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       set_prio();
       --rem;
       const int j0 = jt * BK;
-      const int cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nqa, nka, sminw, smaxw);
+      int cinfo;
+      if constexpr (is_interval(MK)) {
+        cinfo = classify<MK>(a.mask, qw0, qw0 + 31, j0, j0 + BK - 1, nqa, nka, sminw, smaxw);
+      } else {
+        classes_for(jt);
+        cinfo = tc.wave_class(jt);
+      }
       const int cls = cinfo & kClassMask;
-      if (cls == kFull) tile(st, jt, jn, std::false_type{}, false);
-      else if (cls == kPartial) tile(st, jt, jn, std::true_type{}, (cinfo & kCheckBlockMask) != 0);
+      if (cls == kFull) {
+        tile(st, jt, jn, BodyTag<kWhole>{}, false);
+      } else if (cls == kPartial) {
+        // a tile mask that is uniform over the wave's tile leaves only the interval parts
+        if constexpr (MK == kDenseM) tile(st, jt, jn, BodyTag<kPartEl>{}, (cinfo & kCheckBlockMask) != 0);
+        else if constexpr (MK == kBlock) {
+          if (cinfo & kCheckBlockMask) tile(st, jt, jn, BodyTag<kPartEl>{}, true);
+          else tile(st, jt, jn, BodyTag<kPartIv>{}, false);
+        } else {
+          tile(st, jt, jn, BodyTag<kPartIv>{}, false);
+        }
+      }
       else empty_tile(st, jn);
       finish();
     };
@@ -426,10 +457,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : (D == 64 ? 3 : 2)) void dens
       for (; p < fp1; p += 2) {
         set_prio();
         rem -= 2;
-        tile(Stage0{}, jt, jt + 1, std::false_type{}, false);
+        tile(Stage0{}, jt, jt + 1, BodyTag<kWhole>{}, false);
         finish();
         const int jn = next_of(jt + 1);
-        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, std::false_type{}, false);
+        tile(Stage1{}, jt + 1, jn >= 0 ? jn : jt + 1, BodyTag<kWhole>{}, false);
         finish();
         jt = jn;
       }
@@ -480,6 +511,7 @@ template <class E, int D, int NW>
 static int launch_fwd_t(const DenseArgs& a, void* stream) {
   switch (mask_kind(a.mask)) {
     case kArith: return launch_fwd_mk<E, D, NW, kArith>(a, stream);
+    case kLayout: return launch_fwd_mk<E, D, NW, kLayout>(a, stream);
     case kBlock: return launch_fwd_mk<E, D, NW, kBlock>(a, stream);
     default: return launch_fwd_mk<E, D, NW, kDenseM>(a, stream);
   }

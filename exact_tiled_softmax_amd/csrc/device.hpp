@@ -457,13 +457,23 @@ __device__ __forceinline__ unsigned keep_qm_merge(unsigned b0, unsigned b1, int 
 
 // ------------------------------------------------------------ allowed sets
 // Kernels are compiled per mask kind so that the common causal / window case
-// carries no per-element memory lookups:
-//   kArith  causal and look-back window only (plus ragged tails),
-//   kBlock  + the tile mask, read per element only in tiles where it is mixed,
-//   kDenseM + the dense mask.
-enum MaskKind { kArith = 0, kBlock = 1, kDenseM = 2 };
+// carries no per-element memory lookups and no layout bookkeeping:
+//   kArith   causal and look-back window only (plus ragged tails),
+//   kLayout  + variable lengths and row lower bounds (starts): still one key
+//            interval per row,
+//   kBlock   + the tile mask, read per element only in tiles where it is mixed
+//            (lengths and starts handled at run time),
+//   kDenseM  + the dense mask.
+enum MaskKind { kArith = 0, kLayout = 1, kBlock = 2, kDenseM = 3 };
 
-inline int mask_kind(const MaskArgs& m) { return m.dense_mask ? kDenseM : (m.block_mask ? kBlock : kArith); }
+// one allowed-key interval per row (no per-element memory lookups)
+constexpr bool is_interval(int mk) { return mk <= kLayout; }
+
+inline int mask_kind(const MaskArgs& m) {
+  if (m.dense_mask) return kDenseM;
+  if (m.block_mask) return kBlock;
+  return (m.lengths || m.starts) ? kLayout : kArith;
+}
 
 // Per-batch view of the layout parts of the allowed set (variable lengths and
 // packed segments): rows and keys at or past `len` are inactive, and key j is
@@ -473,11 +483,14 @@ struct Layout {
   int len, nka;
   const int32_t* st;
 };
+// (kArith kernels are built for masks without a layout: nothing to read.)
+template <int MK>
 __device__ __forceinline__ Layout layout_of(const MaskArgs& m, int b, int nq, int nk) {
   Layout l;
   l.len = nq;
   l.nka = nk;
   l.st = nullptr;
+  if constexpr (MK == kArith) return l;
   if (m.lengths) {
     l.len = min(max(m.lengths[b], 0), nq);
     l.nka = min(l.len, nk);
@@ -546,11 +559,18 @@ __device__ __forceinline__ void start_range(const int32_t* st, int r0, int r1, i
     lo = min(lo, __shfl_xor(lo, off, 64));
     hi = max(hi, __shfl_xor(hi, off, 64));
   }
-  smin = lo;
-  smax = hi;
+  smin = __builtin_amdgcn_readfirstlane(lo);  // uniform: keep it in a scalar register
+  smax = __builtin_amdgcn_readfirstlane(hi);
 }
 
 enum TileClass { kEmpty = 0, kFull = 1, kPartial = 2, kClassMask = 3, kCheckBlockMask = 4 };
+
+// How a tile's body applies the mask: not at all (every row sees the whole
+// tile), as one allowed-key interval per row (causal, window, lengths, starts;
+// also a tile mask that is uniform over the tile), or element by element.
+enum TileBody { kWhole = 0, kPartIv = 1, kPartEl = 2 };
+template <int T>
+using BodyTag = std::integral_constant<int, T>;
 
 // Classify the rectangle of query rows [ia, ib] x keys [ja, jb] (inclusive;
 // jb may run past nk for a ragged last tile).  Uniform across the wave.
@@ -593,5 +613,36 @@ __device__ __forceinline__ int classify(const MaskArgs& m, int ia, int ib, int j
   if (MK == kDenseM && m.dense_mask) cls = (cls & kCheckBlockMask) | kPartial;
   return cls;
 }
+
+// Classes of 64 consecutive tiles (or dK/dV steps) starting at `base`, one
+// tile per lane, for the mask kinds that read memory to classify (tile and
+// dense masks): the lookups of a whole chunk are issued together instead of a
+// dependent load per tile on the way from one tile to the next.  `nonempty`
+// is the workgroup's rectangle, the other three the calling wave's.  All bits
+// are wave-uniform.
+struct TileClasses {
+  int base;
+  uint64_t nonempty, full, part, cbm;
+  __device__ __forceinline__ void set(int b, int cls_wg, int cls_wave) {
+    base = b;
+    nonempty = __builtin_amdgcn_ballot_w64(cls_wg != kEmpty);
+    full = __builtin_amdgcn_ballot_w64((cls_wave & kClassMask) == kFull);
+    part = __builtin_amdgcn_ballot_w64((cls_wave & kClassMask) == kPartial);
+    cbm = __builtin_amdgcn_ballot_w64((cls_wave & kCheckBlockMask) != 0);
+  }
+  __device__ __forceinline__ bool covers(int t) const { return base >= 0 && t >= base && t < base + 64; }
+  // the wave's class of tile t (covers(t) must hold), in classify()'s encoding
+  __device__ __forceinline__ int wave_class(int t) const {
+    const uint64_t bit = 1ull << (t - base);
+    if (full & bit) return kFull;
+    if (part & bit) return kPartial | ((cbm & bit) ? kCheckBlockMask : 0);
+    return kEmpty;
+  }
+  // first tile >= t of the chunk whose workgroup rectangle is not empty, or -1
+  __device__ __forceinline__ int next_nonempty(int t) const {
+    const uint64_t m = nonempty >> (t - base);
+    return m ? t + (int)__builtin_ctzll(m) : -1;
+  }
+};
 
 }  // namespace ets

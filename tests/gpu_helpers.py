@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import workloads
+from workloads import device
 
 DT = {"f32": 0, "f16": 1, "bf16": 2}
 
@@ -20,26 +21,17 @@ def torch_cuda():
 
 
 def to_dev(storage, dtype):
-    torch = torch_cuda()
-    a = np.ascontiguousarray(storage)
-    if dtype == "bf16":
-        t = torch.from_numpy(a.view(np.int16))
-    else:
-        t = torch.from_numpy(a)
-    return t.to("cuda")
+    torch_cuda()
+    return device.to_dev(storage, dtype)
 
 
 def empty(shape, dtype):
-    torch = torch_cuda()
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.int16}[dtype]
-    return torch.full(shape, 0, dtype=tdt, device="cuda")
+    torch_cuda()
+    return device.empty(shape, dtype)
 
 
 def from_dev(t, dtype):
-    a = t.detach().cpu().numpy()
-    if dtype == "bf16":
-        return workloads.bf16_bits_to_f64(a.view(np.uint16))
-    return a.astype(np.float64)
+    return device.from_dev(t, dtype)
 
 
 def rel_fro(x, ref):
