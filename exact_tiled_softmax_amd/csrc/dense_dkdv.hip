@@ -104,9 +104,13 @@ constexpr int plan_copy_rank(int gi) {  // index of group gi among the copy grou
 // in a fixed order (DkPlan), one MFMA per slot with operands read three slots
 // ahead, so the VALU work of a block runs under the MFMAs of another; the
 // copy of the next step's rows into the other LDS stage is spread over the
-// first group.
+// first group.  d = 128 runs one wave per SIMD (the accumulators and the
+// wave's K, V rows need more than half the register file); d = 64 runs two
+// workgroups per compute unit, whose steps are short enough that a second
+// workgroup hiding the other's memory waits pays for the few registers it
+// spills (measured on the masked workload: 127 -> 108 us).
 template <class E, int D, int MK, bool DROP>
-__global__ __launch_bounds__(256, 1) void dense_bwd_dkdv_kernel(const DenseArgs a, int n_kblocks) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(const DenseArgs a, int n_kblocks) {
   constexpr int BQ = 64;  // query rows per step
   typedef DkPlan<BQ / 32> Plan;
   constexpr int KS = D / 16;
