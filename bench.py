@@ -7,6 +7,8 @@ are seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-probe     # plain device copy of known size, for scaling HBM counters
+    python bench.py --issue-probe    # MFMA rate with 0..12 independent FMAs per MFMA, 1 and 2 waves/SIMD
+    python bench.py --atomic-probe   # fp32 atomic-add rate in the sparse dKV scatter's pattern
 
 The roofline object's "traffic" (HBM bytes per launch of the dominant kernel)
 comes from profiles/<kernel>_<workload>_traffic.md, written from rocprofv3
@@ -128,6 +130,54 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "dispatches": 5}), flush=True)
+
+
+def issue_probe():
+    """MFMA rate this device sustains with K independent fp32 FMAs issued after
+    every MFMA (K = 0 .. 12), at one and two waves per SIMD: how much vector
+    work hides under the matrix instructions.  One JSON line per setting."""
+    import torch
+    import exact_tiled_softmax_amd as ets
+    sink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for wps in (1, 2):
+        for k in (0, 2, 4, 6, 8, 12):
+            ets.attn_issue_probe(wps, k, 64, sink, sink.numel(), stream=stream)  # warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            n = ets.attn_issue_probe(wps, k, 2048, sink, sink.numel(), stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tf = n * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+            print(json.dumps({"probe": "issue", "waves_per_simd": wps, "fma_per_mfma": k, "mfma_TFLOP/s": tf}),
+                  flush=True)
+
+
+def atomic_probe():
+    """fp32 atomic adds per second into random rows of a 16384 x 576 table (the
+    sparse dKV accumulator's shape), checked against the expected counts."""
+    import torch
+    import exact_tiled_softmax_amd as ets
+    rows, n_idx, blocks, gpw = 16384, 1 << 20, 4096, 64
+    g = torch.Generator(device="cpu").manual_seed(0)
+    idx_h = torch.randint(0, rows, (n_idx,), generator=g, dtype=torch.int32)
+    idx = idx_h.cuda()
+    table = torch.zeros(rows, 576, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ets.attn_atomic_probe(table, rows, idx, n_idx, 64, 1, stream=stream)  # warm-up
+    table.zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n = ets.attn_atomic_probe(table, rows, idx, n_idx, blocks, gpw, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    visits = blocks * 4 * gpw * 4
+    want = torch.bincount(idx_h[torch.arange(visits) % n_idx].long(), minlength=rows).float()
+    exact = bool(torch.equal(table.cpu(), want[:, None].expand(rows, 576)))
+    print(json.dumps({"probe": "atomic", "adds": n, "ms": ms, "G_adds/s": n / (ms * 1e-3) / 1e9,
+                      "counts_exact": exact}), flush=True)
 
 
 def mfma_microbench(waves_per_simd=2, iters=4096):
@@ -396,6 +446,8 @@ def main():
     ap.add_argument("--workload", default="dense_causal_bf16_b4h16_n2048_d128", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="run only the reference copy (counter scaling)")
+    ap.add_argument("--issue-probe", action="store_true", help="run only the MFMA + VALU issue probe")
+    ap.add_argument("--atomic-probe", action="store_true", help="run only the fp32 atomic-rate probe")
     ap.add_argument("--no-dropout", action="store_true", help="dense workloads: run the same shape with rate 0")
     ap.add_argument("--deterministic", action="store_true",
                     help="sparse workload: the bit-reproducible dKV backward (attn_sparse_bwd_det)")
@@ -411,6 +463,12 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.issue_probe:
+        issue_probe()
+        return
+    if args.atomic_probe:
+        atomic_probe()
         return
     w = workloads.WORKLOADS[args.workload]
     if isinstance(w, workloads.DenseWorkload):

@@ -20,7 +20,7 @@ __all__ = [
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
     "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_fwd_lse", "attn_sparse_bwd_lse", "attn_sparse_bwd_det", "attn_sparse_bwd_det_workspace_size",
-    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_status_string", "library_path", "lib",
+    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_issue_probe", "attn_atomic_probe", "attn_status_string", "library_path", "lib",
 ]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP, ATTN_ERR_NONFINITE = range(6)
@@ -109,6 +109,10 @@ lib.attn_dropout_mask.restype = _i
 lib.attn_dropout_mask.argtypes = [_f, ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
 lib.attn_mfma_probe.restype = _i
 lib.attn_mfma_probe.argtypes = [_i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
+lib.attn_issue_probe.restype = _i
+lib.attn_issue_probe.argtypes = [_i, _i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
+lib.attn_atomic_probe.restype = _i
+lib.attn_atomic_probe.argtypes = [_vp, _i, _vp, _i, _i, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 
 
 class AttnError(RuntimeError):
@@ -268,4 +272,22 @@ def attn_mfma_probe(waves_per_simd, iters, sink, sink_len, stream=None, raise_on
     st = lib.attn_mfma_probe(int(waves_per_simd), int(iters), _ptr(sink), int(sink_len), ctypes.byref(n),
                              _stream(stream))
     _check(st, "attn_mfma_probe", raise_on_error)
+    return n.value
+
+
+def attn_issue_probe(waves_per_simd, valu_per_mfma, iters, sink, sink_len, stream=None, raise_on_error=True):
+    """Launch the MFMA + VALU issue probe; returns the number of MFMA instructions issued."""
+    n = ctypes.c_longlong(0)
+    st = lib.attn_issue_probe(int(waves_per_simd), int(valu_per_mfma), int(iters), _ptr(sink), int(sink_len),
+                              ctypes.byref(n), _stream(stream))
+    _check(st, "attn_issue_probe", raise_on_error)
+    return n.value
+
+
+def attn_atomic_probe(table, rows, idx, n_idx, blocks, groups_per_wave, stream=None, raise_on_error=True):
+    """Launch the fp32 atomic-add rate probe; returns the number of adds issued."""
+    n = ctypes.c_longlong(0)
+    st = lib.attn_atomic_probe(_ptr(table), int(rows), _ptr(idx), int(n_idx), int(blocks), int(groups_per_wave),
+                               ctypes.byref(n), _stream(stream))
+    _check(st, "attn_atomic_probe", raise_on_error)
     return n.value

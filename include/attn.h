@@ -343,6 +343,30 @@ attn_status attn_dropout_mask(float rate, uint64_t seed, int B, int H, int n_q, 
 attn_status attn_mfma_probe(int waves_per_simd, int iters, float* sink, int sink_len, long long* mfmas,
                             void* stream);
 
+/*
+ * attn_issue_probe -- measurement aid, not part of the method: as
+ * attn_mfma_probe (one workgroup of 4 * waves_per_simd waves per compute unit,
+ * iters x 8 bf16 v_mfma_f32_32x32x16 per wave, four accumulators), with
+ * valu_per_mfma (0, 2, 4, 6, 8 or 12) independent fp32 FMAs issued after each
+ * MFMA, so that the caller can measure how much vector-ALU work the device
+ * hides under matrix instructions.  *mfmas receives the MFMA count.
+ * INVALID_ARG for other valu_per_mfma values and as attn_mfma_probe.
+ */
+attn_status attn_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* sink, int sink_len,
+                             long long* mfmas, void* stream);
+
+/*
+ * attn_atomic_probe -- measurement aid, not part of the method: fp32 atomic
+ * adds of 1.0 into rows of `table` (device, [rows][576] floats, caller-owned
+ * and -initialised), in the sparse dKV scatter's pattern (each instruction
+ * covers 4 rows x 16 consecutive floats; 576 adds per row visit).  blocks
+ * workgroups of 4 waves each visit groups_per_wave x 4 rows per wave, row
+ * numbers taken cyclically from idx[0 .. n_idx) (device int32; entries outside
+ * [0, rows) are skipped).  *adds (host) receives the number of adds issued.
+ */
+attn_status attn_atomic_probe(float* table, int rows, const int32_t* idx, int n_idx, int blocks, int groups_per_wave,
+                              long long* adds, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(attn_status status);
 

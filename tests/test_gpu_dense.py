@@ -272,6 +272,27 @@ def test_mfma_probe_runs_and_counts():
     assert bool(torch.isfinite(sink[:cus]).all())
 
 
+def test_issue_and_atomic_probes_run_and_count():
+    import exact_tiled_softmax_amd as ets
+    torch = gh.torch_cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    assert ets.attn_issue_probe(1, 4, 8, sink, sink.numel()) == cus * 4 * 8 * 8
+    assert ets.attn_issue_probe(2, 7, 8, sink, sink.numel(), raise_on_error=False) == 0  # 7: not built
+    rows = 50
+    table = torch.zeros(rows, 576, dtype=torch.float32, device="cuda")
+    idx = torch.tensor([3, 49, 3, -1, 60, 0, 7, 3], dtype=torch.int32, device="cuda")
+    n = ets.attn_atomic_probe(table, rows, idx, idx.numel(), 2, 1)
+    torch.cuda.synchronize()
+    assert n == 2 * 4 * 1 * 4 * 576
+    counts = torch.zeros(rows)
+    for k in range(32):  # 2 blocks x 4 waves x 1 group x 4 rows, indices taken cyclically
+        r = int(idx[k % 8])
+        if 0 <= r < rows:
+            counts[r] += 1
+    assert torch.equal(table.cpu(), counts[:, None].expand(rows, 576))
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
 def test_backward_phases_reproduce_attn_bwd(dtype, d):
     # attn_bwd_phase(1), (2), (4) in turn run the same kernels on the same
