@@ -143,3 +143,32 @@ def test_sparse_deterministic_dkv_is_bit_reproducible():
     assert gh.rel_fro(r1["dKV"], dKV) <= REL_TOL
     assert gh.rel_fro(r1["dKV"], ref["dKV"]) <= 1e-2
 
+
+@pytest.mark.parametrize("log2_scale", [-20, -30])
+def test_sparse_deterministic_dkv_absolute_error_bound(log2_scale):
+    # The fixed-point mode rounds each per-token contribution to dKV to a
+    # multiple of 2^-32, so its absolute error is at most (selections of the
+    # row) * 2^-33 beyond the fp32 path; at small gradient scales that bound is
+    # what limits it.  dO is scaled by a power of two, which is exact in bf16.
+    c = _case(40, 300, 120, "bf16", 9, dup=True)
+    alpha = 1.0 / 24.0
+    s = 2.0 ** log2_scale
+    dO, dO64 = workloads.round_to(c["dO64"] * s, "bf16")
+    assert np.array_equal(dO64, c["dO64"] * s)
+    det = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=dO, det=True)
+    ref = gh.sparse_run("bf16", c["Q"], c["KV"], c["idx"], c["L"], c["sink"], alpha, dO=dO)
+    cnt = np.zeros(c["KV"].shape[0])
+    for t in range(c["idx"].shape[0]):
+        np.add.at(cnt, c["idx"][t, :c["L"][t]], 1.0)
+    a, b = det["dKV"], ref["dKV"]
+    # one bf16 ulp (2^-7 relative) for the two final roundings, a small
+    # allowance for the order-dependent fp32 sums of the atomic path, plus the
+    # fixed-point bound of the row
+    tol = (2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 2.0 ** -16 * np.abs(b).max()
+           + cnt[:, None] * 2.0 ** -33)
+    assert np.all(np.abs(a - b) <= tol)
+    assert np.all(a[cnt == 0] == 0)
+    if log2_scale == -20:
+        sink64 = c["sink"].astype(np.float64)
+        _, dKV, _ = sparse.vjp(c["Q64"], c["KV64"], c["idx"], c["L"], sink64, alpha, DV, dO64)
+        assert gh.rel_fro(det["dKV"], dKV) <= REL_TOL
