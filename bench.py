@@ -9,6 +9,7 @@ are seeded synthetic tensors already resident in HBM.  Prints ONE JSON line.
     python bench.py --copy-probe     # plain device copy of known size, for scaling HBM counters
     python bench.py --issue-probe    # MFMA rate with 0..12 independent FMAs per MFMA, 1 and 2 waves/SIMD
     python bench.py --atomic-probe   # fp32 atomic-add rate in the sparse dKV scatter's pattern
+    python bench.py --lds-probe      # LDS read bandwidth with 4, 8 and 16 waves per compute unit
 
 The roofline object's "traffic" (HBM bytes per launch of the dominant kernel)
 comes from profiles/<kernel>_<workload>_traffic.md, written from rocprofv3
@@ -178,6 +179,25 @@ def atomic_probe():
     exact = bool(torch.equal(table.cpu(), want[:, None].expand(rows, 576)))
     print(json.dumps({"probe": "atomic", "adds": n, "ms": ms, "G_adds/s": n / (ms * 1e-3) / 1e9,
                       "counts_exact": exact}), flush=True)
+
+
+def lds_probe():
+    """LDS read bytes per second and per compute unit, 4 / 8 / 16 waves per CU."""
+    import torch
+    import exact_tiled_softmax_amd as ets
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for waves in (4, 8, 16):
+        ets.attn_lds_probe(waves, 16, sink, sink.numel(), stream=stream)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        n = ets.attn_lds_probe(waves, 4096, sink, sink.numel(), stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        print(json.dumps({"probe": "lds", "waves_per_cu": waves, "bytes": n, "ms": ms,
+                          "TB/s": n / (ms * 1e-3) / 1e12, "GB/s_per_cu": n / (ms * 1e-3) / 1e9 / cus}), flush=True)
 
 
 def mfma_microbench(waves_per_simd=2, iters=4096):
@@ -448,6 +468,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run only the reference copy (counter scaling)")
     ap.add_argument("--issue-probe", action="store_true", help="run only the MFMA + VALU issue probe")
     ap.add_argument("--atomic-probe", action="store_true", help="run only the fp32 atomic-rate probe")
+    ap.add_argument("--lds-probe", action="store_true", help="run only the LDS read-bandwidth probe")
     ap.add_argument("--no-dropout", action="store_true", help="dense workloads: run the same shape with rate 0")
     ap.add_argument("--deterministic", action="store_true",
                     help="sparse workload: the bit-reproducible dKV backward (attn_sparse_bwd_det)")
@@ -469,6 +490,9 @@ def main():
         return
     if args.atomic_probe:
         atomic_probe()
+        return
+    if args.lds_probe:
+        lds_probe()
         return
     w = workloads.WORKLOADS[args.workload]
     if isinstance(w, workloads.DenseWorkload):

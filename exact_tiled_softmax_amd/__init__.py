@@ -20,7 +20,7 @@ __all__ = [
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
     "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_fwd_lse", "attn_sparse_bwd_lse", "attn_sparse_bwd_det", "attn_sparse_bwd_det_workspace_size",
-    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_issue_probe", "attn_atomic_probe", "attn_status_string", "library_path", "lib",
+    "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_issue_probe", "attn_atomic_probe", "attn_lds_probe", "attn_status_string", "library_path", "lib",
 ]
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP, ATTN_ERR_NONFINITE = range(6)
@@ -113,6 +113,8 @@ lib.attn_issue_probe.restype = _i
 lib.attn_issue_probe.argtypes = [_i, _i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 lib.attn_atomic_probe.restype = _i
 lib.attn_atomic_probe.argtypes = [_vp, _i, _vp, _i, _i, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
+lib.attn_lds_probe.restype = _i
+lib.attn_lds_probe.argtypes = [_i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 
 
 class AttnError(RuntimeError):
@@ -290,4 +292,13 @@ def attn_atomic_probe(table, rows, idx, n_idx, blocks, groups_per_wave, stream=N
     st = lib.attn_atomic_probe(_ptr(table), int(rows), _ptr(idx), int(n_idx), int(blocks), int(groups_per_wave),
                                ctypes.byref(n), _stream(stream))
     _check(st, "attn_atomic_probe", raise_on_error)
+    return n.value
+
+
+def attn_lds_probe(waves_per_cu, iters, sink, sink_len, stream=None, raise_on_error=True):
+    """Launch the LDS read-bandwidth probe; returns the bytes read from LDS."""
+    n = ctypes.c_longlong(0)
+    st = lib.attn_lds_probe(int(waves_per_cu), int(iters), _ptr(sink), int(sink_len), ctypes.byref(n),
+                            _stream(stream))
+    _check(st, "attn_lds_probe", raise_on_error)
     return n.value

@@ -466,4 +466,12 @@ attn_status attn_atomic_probe(float* table, int rows, const int32_t* idx, int n_
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+attn_status attn_lds_probe(int waves_per_cu, int iters, uint32_t* sink, int sink_len, long long* bytes, void* stream) {
+  if ((waves_per_cu != 4 && waves_per_cu != 8 && waves_per_cu != 16) || iters < 1 || !sink || !bytes || sink_len < 1)
+    return ATTN_ERR_INVALID_ARG;
+  const int rc = launch_lds_probe(waves_per_cu, iters, sink, sink_len, bytes, stream);
+  if (rc == -1) return ATTN_ERR_INVALID_ARG;  // sink shorter than the CU count
+  return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 }  // extern "C"

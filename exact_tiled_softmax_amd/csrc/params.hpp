@@ -93,6 +93,7 @@ int launch_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* 
                        long long* mfmas, void* stream);
 int launch_atomic_probe(float* table, int rows, const int32_t* idx, int n_idx, int blocks, int groups_per_wave,
                         long long* adds, void* stream);
+int launch_lds_probe(int waves, int iters, uint32_t* sink, int sink_len, long long* bytes, void* stream);
 
 // Debug checks (debug.hip).  Each returns 0 or a hipError_t value and sets
 // *bad (host) when the check fails; each synchronises the stream.

@@ -135,4 +135,36 @@ int launch_atomic_probe(float* table, int rows, const int32_t* idx, int n_idx, i
   return 0;
 }
 
+// Measurement aid: LDS read bandwidth.  One workgroup of `waves` waves per
+// compute unit fills 64 KiB of LDS, then every wave issues iters x 16
+// conflict-free ds_read_b128 (lane l reads 16 bytes at 16 l + 1 KiB k, all
+// addresses inside the 64 KiB array) and XOR-folds them into sink.
+__global__ __launch_bounds__(1024) void lds_probe_kernel(int iters, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) char buf[65536];
+  for (int i = threadIdx.x; i < 65536 / 4; i += blockDim.x) ((uint32_t*)buf)[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t base = (uint32_t)(lane * 16 + wave * 8192) & 0xFFFFu;
+  u32x4 acc = u32x4{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t addr = (base + (uint32_t)k * 1024u + (uint32_t)it * 64u) & 0xFFF0u;
+      acc ^= *(const u32x4*)(buf + addr);
+    }
+  }
+  const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (threadIdx.x == 0) sink[blockIdx.x] = x;  // keeps the loads alive
+}
+
+int launch_lds_probe(int waves, int iters, uint32_t* sink, int sink_len, long long* bytes, void* stream) {
+  int dev = 0, cus = 0;
+  ETS_TRY(hipGetDevice(&dev));
+  ETS_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (cus > sink_len) return -1;
+  *bytes = (long long)cus * waves * 64 * 16 * 16 * iters;
+  ETS_TRY(launch(lds_probe_kernel, dim3(cus), dim3(64 * waves), 0, (hipStream_t)stream, iters, sink));
+  return 0;
+}
+
 }  // namespace ets

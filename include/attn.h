@@ -367,6 +367,17 @@ attn_status attn_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, f
 attn_status attn_atomic_probe(float* table, int rows, const int32_t* idx, int n_idx, int blocks, int groups_per_wave,
                               long long* adds, void* stream);
 
+/*
+ * attn_lds_probe -- measurement aid, not part of the method: one workgroup of
+ * waves_per_cu (4, 8 or 16) waves on every compute unit fills 64 KiB of LDS,
+ * then each wave issues iters x 16 conflict-free 16-byte-per-lane LDS reads,
+ * so that the caller can time the launch and report the LDS read bandwidth
+ * the device sustains.  sink: device uint32 buffer of sink_len >= number of
+ * compute units.  *bytes (host) receives the bytes read from LDS.
+ * INVALID_ARG for other wave counts, iters < 1, null pointers or a short sink.
+ */
+attn_status attn_lds_probe(int waves_per_cu, int iters, uint32_t* sink, int sink_len, long long* bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(attn_status status);
 

@@ -148,7 +148,7 @@ def test_mfma_probe_rejects_bad_arguments():
         assert st == ets.ATTN_ERR_INVALID_ARG
 
 
-def test_issue_and_atomic_probes_reject_bad_arguments():
+def test_issue_atomic_and_lds_probes_reject_bad_arguments():
     import ctypes
     import exact_tiled_softmax_amd as ets
     cnt = ctypes.c_longlong(0)
@@ -158,6 +158,8 @@ def test_issue_and_atomic_probes_reject_bad_arguments():
                                                (P, 8, P, 0, 1, 1), (P, 8, P, 4, 0, 1), (P, 8, P, 4, 1, 0)):
         st = ets.lib.attn_atomic_probe(ets._ptr(tab), rows, ets._ptr(idx), n_idx, blocks, gpw, ctypes.byref(cnt), None)
         assert st == ets.ATTN_ERR_INVALID_ARG
+    for w, it, sink, n in ((2, 10, P, 256), (32, 10, P, 256), (8, 0, P, 256), (8, 10, None, 256), (8, 10, P, 0)):
+        assert ets.lib.attn_lds_probe(w, it, ets._ptr(sink), n, ctypes.byref(cnt), None) == ets.ATTN_ERR_INVALID_ARG
 
 
 def test_one_hip_runtime_per_process():

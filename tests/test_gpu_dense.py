@@ -293,6 +293,28 @@ def test_issue_and_atomic_probes_run_and_count():
     assert torch.equal(table.cpu(), counts[:, None].expand(rows, 576))
 
 
+def test_lds_probe_reads_what_it_wrote():
+    # the probe's LDS words are i * 2654435761 mod 2^32; workgroup w's first
+    # lane XOR-folds the 16-byte reads at (1 KiB k + 64 it) mod 64 KiB
+    import exact_tiled_softmax_amd as ets
+    torch = gh.torch_cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    iters = 40
+    n = ets.attn_lds_probe(8, iters, sink, sink.numel())
+    torch.cuda.synchronize()
+    assert n == cus * 8 * 64 * 16 * 16 * iters
+    words = (np.arange(16384, dtype=np.uint64) * 2654435761) % (1 << 32)
+    acc = 0
+    for it in range(iters):
+        for k in range(16):
+            a = ((k * 1024 + it * 64) & 0xFFF0) // 4
+            for w in range(4):
+                acc ^= int(words[a + w])
+    got = sink[:cus].cpu().numpy().view(np.uint32)
+    assert np.all(got == acc)
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
 def test_backward_phases_reproduce_attn_bwd(dtype, d):
     # attn_bwd_phase(1), (2), (4) in turn run the same kernels on the same
