@@ -134,51 +134,63 @@ def copy_probe():
 
 
 def issue_probe():
-    """MFMA rate this device sustains with K independent fp32 FMAs issued after
-    every MFMA (K = 0 .. 12), at one and two waves per SIMD: how much vector
-    work hides under the matrix instructions.  One JSON line per setting."""
+    """MFMA rate this device sustains with K independent fp32 FMAs, or K
+    independent base-2 exponentials, issued after every MFMA (K = 0 .. 12), at
+    one and two waves per SIMD: how much vector work hides under the matrix
+    instructions.  One JSON line per setting."""
     import torch
     import exact_tiled_softmax_amd as ets
     sink = torch.empty(4096, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    for wps in (1, 2):
-        for k in (0, 2, 4, 6, 8, 12):
-            ets.attn_issue_probe(wps, k, 64, sink, sink.numel(), stream=stream)  # warm-up
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            n = ets.attn_issue_probe(wps, k, 2048, sink, sink.numel(), stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            tf = n * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
-            print(json.dumps({"probe": "issue", "waves_per_simd": wps, "fma_per_mfma": k, "mfma_TFLOP/s": tf}),
-                  flush=True)
+    for trans, kind in ((0, "fma"), (1, "exp")):
+        for wps in (1, 2):
+            for k in (0, 2, 4, 6, 8, 12):
+                ets.attn_issue_probe(wps, k, trans, 64, sink, sink.numel(), stream=stream)  # warm-up
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                n = ets.attn_issue_probe(wps, k, trans, 2048, sink, sink.numel(), stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                tf = n * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+                print(json.dumps({"probe": "issue", "waves_per_simd": wps, "kind": kind, "per_mfma": k,
+                                  "mfma_TFLOP/s": tf}), flush=True)
 
 
 def atomic_probe():
-    """fp32 atomic adds per second into random rows of a 16384 x 576 table (the
-    sparse dKV accumulator's shape), checked against the expected counts."""
+    """fp32 atomic adds per second into rows of a [rows x 576] table, checked
+    against the expected counts: random rows of a 16384-row table (the sparse
+    dKV accumulator's shape, 37.7 MB), random rows of 1024- and 64-row tables
+    (2.4 MB and 147 KB, small enough to stay in one XCD's 4 MB L2), and the
+    16384 rows in order (the pattern of a contiguous accumulator such as a
+    dQ tile)."""
     import torch
     import exact_tiled_softmax_amd as ets
-    rows, n_idx, blocks, gpw = 16384, 1 << 20, 4096, 64
-    g = torch.Generator(device="cpu").manual_seed(0)
-    idx_h = torch.randint(0, rows, (n_idx,), generator=g, dtype=torch.int32)
-    idx = idx_h.cuda()
-    table = torch.zeros(rows, 576, dtype=torch.float32, device="cuda")
+    n_idx, blocks, gpw = 1 << 20, 4096, 64
     stream = torch.cuda.current_stream()
-    ets.attn_atomic_probe(table, rows, idx, n_idx, 64, 1, stream=stream)  # warm-up
-    table.zero_()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    n = ets.attn_atomic_probe(table, rows, idx, n_idx, blocks, gpw, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    visits = blocks * 4 * gpw * 4
-    want = torch.bincount(idx_h[torch.arange(visits) % n_idx].long(), minlength=rows).float()
-    exact = bool(torch.equal(table.cpu(), want[:, None].expand(rows, 576)))
-    print(json.dumps({"probe": "atomic", "adds": n, "ms": ms, "G_adds/s": n / (ms * 1e-3) / 1e9,
-                      "counts_exact": exact}), flush=True)
+    for name, rows, order in (("random", 16384, "random"), ("random", 1024, "random"), ("random", 64, "random"),
+                              ("sequential", 16384, "sequential")):
+        g = torch.Generator(device="cpu").manual_seed(0)
+        if order == "random":
+            idx_h = torch.randint(0, rows, (n_idx,), generator=g, dtype=torch.int32)
+        else:
+            idx_h = (torch.arange(n_idx, dtype=torch.int32) % rows).to(torch.int32)
+        idx = idx_h.cuda()
+        table = torch.zeros(rows, 576, dtype=torch.float32, device="cuda")
+        ets.attn_atomic_probe(table, rows, idx, n_idx, 64, 1, stream=stream)  # warm-up
+        table.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        n = ets.attn_atomic_probe(table, rows, idx, n_idx, blocks, gpw, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        visits = blocks * 4 * gpw * 4
+        want = torch.bincount(idx_h[torch.arange(visits) % n_idx].long(), minlength=rows).float()
+        exact = bool(torch.equal(table.cpu(), want[:, None].expand(rows, 576)))
+        print(json.dumps({"probe": "atomic", "rows": rows, "order": order, "table_MB": rows * 576 * 4 / 1e6,
+                          "adds": n, "ms": ms, "G_adds/s": n / (ms * 1e-3) / 1e9, "counts_exact": exact}),
+              flush=True)
 
 
 def lds_probe():

@@ -110,7 +110,7 @@ lib.attn_dropout_mask.argtypes = [_f, ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
 lib.attn_mfma_probe.restype = _i
 lib.attn_mfma_probe.argtypes = [_i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 lib.attn_issue_probe.restype = _i
-lib.attn_issue_probe.argtypes = [_i, _i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
+lib.attn_issue_probe.argtypes = [_i, _i, _i, _i, _vp, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 lib.attn_atomic_probe.restype = _i
 lib.attn_atomic_probe.argtypes = [_vp, _i, _vp, _i, _i, _i, ctypes.POINTER(ctypes.c_longlong), _vp]
 lib.attn_lds_probe.restype = _i
@@ -277,11 +277,11 @@ def attn_mfma_probe(waves_per_simd, iters, sink, sink_len, stream=None, raise_on
     return n.value
 
 
-def attn_issue_probe(waves_per_simd, valu_per_mfma, iters, sink, sink_len, stream=None, raise_on_error=True):
+def attn_issue_probe(waves_per_simd, valu_per_mfma, trans, iters, sink, sink_len, stream=None, raise_on_error=True):
     """Launch the MFMA + VALU issue probe; returns the number of MFMA instructions issued."""
     n = ctypes.c_longlong(0)
-    st = lib.attn_issue_probe(int(waves_per_simd), int(valu_per_mfma), int(iters), _ptr(sink), int(sink_len),
-                              ctypes.byref(n), _stream(stream))
+    st = lib.attn_issue_probe(int(waves_per_simd), int(valu_per_mfma), int(trans), int(iters), _ptr(sink),
+                              int(sink_len), ctypes.byref(n), _stream(stream))
     _check(st, "attn_issue_probe", raise_on_error)
     return n.value
 

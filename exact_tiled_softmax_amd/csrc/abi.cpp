@@ -445,14 +445,15 @@ attn_status attn_mfma_probe(int waves_per_simd, int iters, float* sink, int sink
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-attn_status attn_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* sink, int sink_len,
+attn_status attn_issue_probe(int waves_per_simd, int valu_per_mfma, int trans, int iters, float* sink, int sink_len,
                              long long* mfmas, void* stream) {
   if ((waves_per_simd != 1 && waves_per_simd != 2) || iters < 1 || !sink || !mfmas || sink_len < 1)
     return ATTN_ERR_INVALID_ARG;
+  if (trans != 0 && trans != 1) return ATTN_ERR_INVALID_ARG;
   if (valu_per_mfma != 0 && valu_per_mfma != 2 && valu_per_mfma != 4 && valu_per_mfma != 6 && valu_per_mfma != 8 &&
       valu_per_mfma != 12)
     return ATTN_ERR_INVALID_ARG;
-  const int rc = launch_issue_probe(waves_per_simd, valu_per_mfma, iters, sink, sink_len, mfmas, stream);
+  const int rc = launch_issue_probe(waves_per_simd, valu_per_mfma, trans, iters, sink, sink_len, mfmas, stream);
   if (rc == -1) return ATTN_ERR_INVALID_ARG;  // sink shorter than the CU count
   return rc == 0 ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -89,7 +89,7 @@ int launch_sparse_fwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_sparse_bwd(const SparseArgs& a, Dt dt, void* stream);
 int launch_dropout_mask(const DropArgs& d, int B, int H, int nq, int nk, uint8_t* xi, void* stream);
 int launch_mfma_probe(int waves_per_simd, int iters, float* sink, int sink_len, long long* mfmas, void* stream);
-int launch_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* sink, int sink_len,
+int launch_issue_probe(int waves_per_simd, int valu_per_mfma, int trans, int iters, float* sink, int sink_len,
                        long long* mfmas, void* stream);
 int launch_atomic_probe(float* table, int rows, const int32_t* idx, int n_idx, int blocks, int groups_per_wave,
                         long long* adds, void* stream);

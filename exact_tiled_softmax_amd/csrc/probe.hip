@@ -47,9 +47,13 @@ namespace ets {
 
 // Measurement aid: how many independent VALU instructions this device hides
 // under MFMAs.  Each wave issues iters x 8 v_mfma_f32_32x32x16_bf16 (four
-// accumulators), each followed by K independent v_fma_f32 on registers of
-// their own, the order pinned by scheduling groups.
-template <int K>
+// accumulators), each followed by K independent v_fma_f32 (TRANS = false) or
+// K independent v_exp_f32 (TRANS = true) on registers of their own, the order
+// pinned by scheduling groups.  (The exponentials run to infinity after a few
+// steps; the rate does not depend on the values.)
+constexpr int kSchedTrans = 0x400;  // scheduling-group mask of transcendental instructions
+
+template <int K, bool TRANS>
 __global__ __launch_bounds__(512) void issue_probe_kernel(int iters, float* sink) {
   f32x16 acc[4];
 #pragma unroll
@@ -72,10 +76,11 @@ __global__ __launch_bounds__(512) void issue_probe_kernel(int iters, float* sink
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         float& t = v[(m * K + k) & 15];
-        t = fmaf(t, 0.999f, 0.001f);
+        if constexpr (TRANS) t = fast_exp2(t);
+        else t = fmaf(t, 0.999f, 0.001f);
       }
       ETS_SCHED(kSchedMFMA, 1);
-      if constexpr (K > 0) ETS_SCHED(kSchedVALU, K);
+      if constexpr (K > 0) ETS_SCHED(TRANS ? kSchedTrans : kSchedVALU, K);
     }
   }
   float s = 0.f;
@@ -88,7 +93,21 @@ __global__ __launch_bounds__(512) void issue_probe_kernel(int iters, float* sink
   if (threadIdx.x == 0) sink[blockIdx.x] = s;  // keeps the work alive
 }
 
-int launch_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* sink, int sink_len,
+template <bool TRANS>
+static int launch_issue_k(int k, int cus, int threads, int iters, float* sink, hipStream_t st) {
+  switch (k) {
+    case 0: ETS_TRY(launch(issue_probe_kernel<0, TRANS>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
+    case 2: ETS_TRY(launch(issue_probe_kernel<2, TRANS>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
+    case 4: ETS_TRY(launch(issue_probe_kernel<4, TRANS>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
+    case 6: ETS_TRY(launch(issue_probe_kernel<6, TRANS>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
+    case 8: ETS_TRY(launch(issue_probe_kernel<8, TRANS>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
+    case 12: ETS_TRY(launch(issue_probe_kernel<12, TRANS>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
+    default: return -2;
+  }
+  return 0;
+}
+
+int launch_issue_probe(int waves_per_simd, int valu_per_mfma, int trans, int iters, float* sink, int sink_len,
                        long long* mfmas, void* stream) {
   int dev = 0, cus = 0;
   ETS_TRY(hipGetDevice(&dev));
@@ -97,18 +116,9 @@ int launch_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* 
   const int threads = 256 * waves_per_simd;
   *mfmas = (long long)cus * (threads / 64) * iters * 8;
   hipStream_t st = (hipStream_t)stream;
-  switch (valu_per_mfma) {
-    case 0: ETS_TRY(launch(issue_probe_kernel<0>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
-    case 2: ETS_TRY(launch(issue_probe_kernel<2>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
-    case 4: ETS_TRY(launch(issue_probe_kernel<4>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
-    case 6: ETS_TRY(launch(issue_probe_kernel<6>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
-    case 8: ETS_TRY(launch(issue_probe_kernel<8>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
-    case 12: ETS_TRY(launch(issue_probe_kernel<12>, dim3(cus), dim3(threads), 0, st, iters, sink)); break;
-    default: return -2;
-  }
-  return 0;
+  return trans ? launch_issue_k<true>(valu_per_mfma, cus, threads, iters, sink, st)
+               : launch_issue_k<false>(valu_per_mfma, cus, threads, iters, sink, st);
 }
-
 // Measurement aid: the rate of fp32 atomic adds into random 576-float rows of
 // a table, in the access pattern of the sparse dKV scatter: each instruction
 // covers 4 rows x 16 consecutive floats (16 lanes per row), 36 instructions

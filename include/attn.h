@@ -347,12 +347,13 @@ attn_status attn_mfma_probe(int waves_per_simd, int iters, float* sink, int sink
  * attn_issue_probe -- measurement aid, not part of the method: as
  * attn_mfma_probe (one workgroup of 4 * waves_per_simd waves per compute unit,
  * iters x 8 bf16 v_mfma_f32_32x32x16 per wave, four accumulators), with
- * valu_per_mfma (0, 2, 4, 6, 8 or 12) independent fp32 FMAs issued after each
- * MFMA, so that the caller can measure how much vector-ALU work the device
- * hides under matrix instructions.  *mfmas receives the MFMA count.
- * INVALID_ARG for other valu_per_mfma values and as attn_mfma_probe.
+ * valu_per_mfma (0, 2, 4, 6, 8 or 12) independent vector instructions issued
+ * after each MFMA: fp32 FMAs (trans = 0) or base-2 exponentials, v_exp_f32
+ * (trans = 1), so that the caller can measure how much vector-ALU work the
+ * device hides under matrix instructions.  *mfmas receives the MFMA count.
+ * INVALID_ARG for other valu_per_mfma or trans values and as attn_mfma_probe.
  */
-attn_status attn_issue_probe(int waves_per_simd, int valu_per_mfma, int iters, float* sink, int sink_len,
+attn_status attn_issue_probe(int waves_per_simd, int valu_per_mfma, int trans, int iters, float* sink, int sink_len,
                              long long* mfmas, void* stream);
 
 /*

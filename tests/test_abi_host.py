@@ -152,8 +152,10 @@ def test_issue_atomic_and_lds_probes_reject_bad_arguments():
     import ctypes
     import exact_tiled_softmax_amd as ets
     cnt = ctypes.c_longlong(0)
-    for w, k, it, sink, n in ((3, 0, 10, P, 256), (1, 5, 10, P, 256), (1, 4, 0, P, 256), (2, 4, 10, None, 256)):
-        assert ets.lib.attn_issue_probe(w, k, it, ets._ptr(sink), n, ctypes.byref(cnt), None) == ets.ATTN_ERR_INVALID_ARG
+    for w, k, tr, it, sink, n in ((3, 0, 0, 10, P, 256), (1, 5, 0, 10, P, 256), (1, 4, 0, 0, P, 256),
+                                  (2, 4, 0, 10, None, 256), (1, 4, 2, 10, P, 256), (1, 4, -1, 10, P, 256)):
+        st = ets.lib.attn_issue_probe(w, k, tr, it, ets._ptr(sink), n, ctypes.byref(cnt), None)
+        assert st == ets.ATTN_ERR_INVALID_ARG
     for tab, rows, idx, n_idx, blocks, gpw in ((None, 8, P, 4, 1, 1), (P, 0, P, 4, 1, 1), (P, 8, None, 4, 1, 1),
                                                (P, 8, P, 0, 1, 1), (P, 8, P, 4, 0, 1), (P, 8, P, 4, 1, 0)):
         st = ets.lib.attn_atomic_probe(ets._ptr(tab), rows, ets._ptr(idx), n_idx, blocks, gpw, ctypes.byref(cnt), None)

@@ -277,8 +277,10 @@ def test_issue_and_atomic_probes_run_and_count():
     torch = gh.torch_cuda()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
-    assert ets.attn_issue_probe(1, 4, 8, sink, sink.numel()) == cus * 4 * 8 * 8
-    assert ets.attn_issue_probe(2, 7, 8, sink, sink.numel(), raise_on_error=False) == 0  # 7: not built
+    assert ets.attn_issue_probe(1, 4, 0, 8, sink, sink.numel()) == cus * 4 * 8 * 8
+    assert ets.attn_issue_probe(2, 6, 1, 8, sink, sink.numel()) == cus * 8 * 8 * 8
+    torch.cuda.synchronize()
+    assert ets.attn_issue_probe(2, 7, 0, 8, sink, sink.numel(), raise_on_error=False) == 0  # 7: not built
     rows = 50
     table = torch.zeros(rows, 576, dtype=torch.float32, device="cuda")
     idx = torch.tensor([3, 49, 3, -1, 60, 0, 7, 3], dtype=torch.int32, device="cuda")
