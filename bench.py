@@ -291,12 +291,17 @@ def bench_dense(w, args):
     Y = gh.empty((w.B, w.H, w.n, w.dv), w.dtype)
     LSE = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device="cuda")
     dQ, dK, dV = gh.empty(Q.shape, w.dtype), gh.empty(K.shape, w.dtype), gh.empty(V.shape, w.dtype)
-    ws_bytes = ets.attn_bwd_workspace_size(dt, w.B, w.H, w.H_kv, w.n, w.n, w.d, w.dv)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     mask = {"causal": int(w.causal), "window": w.window, "block_q": w.mask_tile, "block_k": w.mask_tile}
     if block_mask is not None:
         mask["block_mask"] = gh.to_dev(block_mask, "u8")
     drop = (w.rho, w.drop_seed) if w.rho > 0 else None
+    # the workspace of the backward's fastest form for this mask and dropout
+    # (the stored-gamma form with dropout and a causal / window mask;
+    # --recompute-dq: the minimal workspace, the dQ kernel recomputes)
+    ws_size = ets.attn_bwd_workspace_size if args.recompute_dq else (
+        lambda *s: ets.attn_bwd_workspace_size_fast(*s, mask, drop))
+    ws_bytes = ws_size(dt, w.B, w.H, w.H_kv, w.n, w.n, w.d, w.dv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     shape = (dt, w.B, w.H, w.H_kv, w.n, w.n, w.d, w.dv)
     stream = torch.cuda.current_stream()
 
@@ -362,7 +367,9 @@ def bench_dense(w, args):
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), workloads module)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "kv_heads": w.H_kv, "seq_len": w.n,
                    "head_dim": w.d, "causal": w.causal, "window": w.window,
-                   "tile_mask_p": w.block_mask_p, "dropout": w.rho, "allowed_pairs": pairs},
+                   "tile_mask_p": w.block_mask_p, "dropout": w.rho, "allowed_pairs": pairs,
+                   "dq_form": ("stored_gamma" if ws_bytes > ets.attn_bwd_workspace_size(*shape) else "recompute"),
+                   "workspace_bytes": ws_bytes},
         "frac_peak": value / peak,
         "fwd": {"ms": kern_ms["fwd"], "TFLOP/s": fwd_tf, "frac_peak": fwd_tf / peak},
         "bwd": {"ms": bwd_ms, "TFLOP/s": bwd_tf, "frac_peak": bwd_tf / peak},
@@ -482,6 +489,8 @@ def main():
     ap.add_argument("--atomic-probe", action="store_true", help="run only the fp32 atomic-rate probe")
     ap.add_argument("--lds-probe", action="store_true", help="run only the LDS read-bandwidth probe")
     ap.add_argument("--no-dropout", action="store_true", help="dense workloads: run the same shape with rate 0")
+    ap.add_argument("--recompute-dq", action="store_true",
+                    help="dense workloads with dropout: the minimal backward workspace (the dQ kernel recomputes)")
     ap.add_argument("--deterministic", action="store_true",
                     help="sparse workload: the bit-reproducible dKV backward (attn_sparse_bwd_det)")
     args = ap.parse_args()

@@ -18,7 +18,7 @@ __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP",
     "ATTN_ERR_NONFINITE",
     "ATTN_F32", "ATTN_F16", "ATTN_BF16", "ATTN_LSE_TOTAL", "ATTN_LSE_KV", "AttnError", "Mask", "Dropout",
-    "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_sparse_fwd", "attn_sparse_bwd",
+    "attn_fwd", "attn_bwd", "attn_bwd_phase", "attn_bwd_noalloc", "attn_bwd_workspace_size", "attn_bwd_workspace_size_fast", "attn_sparse_fwd", "attn_sparse_bwd",
     "attn_sparse_fwd_lse", "attn_sparse_bwd_lse", "attn_sparse_bwd_det", "attn_sparse_bwd_det_workspace_size",
     "attn_sparse_bwd_workspace_size", "attn_dropout_mask", "attn_mfma_probe", "attn_issue_probe", "attn_atomic_probe", "attn_lds_probe", "attn_status_string", "library_path", "lib",
 ]
@@ -85,6 +85,8 @@ lib.attn_fwd.restype = _i
 lib.attn_fwd.argtypes = [_i] + [_i] * 7 + [_vp] * 3 + [_pm, _f, _i, _pd, _vp, _vp, _vp]
 lib.attn_bwd_workspace_size.restype = _sz
 lib.attn_bwd_workspace_size.argtypes = [_i] * 8
+lib.attn_bwd_workspace_size_fast.restype = _sz
+lib.attn_bwd_workspace_size_fast.argtypes = [_i] * 8 + [_pm, _pd]
 lib.attn_bwd.restype = _i
 lib.attn_bwd.argtypes = ([_i] + [_i] * 7 + [_vp] * 6 + [_pm, _f, _i, _pd] + [_vp] * 3 + [_vp, _sz, _vp])
 lib.attn_bwd_noalloc.restype = _i
@@ -182,6 +184,10 @@ def attn_fwd(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, mask, scale, block_b, dro
 
 def attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv):
     return lib.attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv)
+
+
+def attn_bwd_workspace_size_fast(dt, B, H, H_kv, n_q, n_k, d, dv, mask, dropout):
+    return lib.attn_bwd_workspace_size_fast(dt, B, H, H_kv, n_q, n_k, d, dv, _mask(mask), _drop(dropout))
 
 
 def attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout,

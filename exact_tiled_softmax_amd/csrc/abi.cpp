@@ -179,6 +179,39 @@ size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, i
   return 2 * round_up(((size_t)B * H * n_q + 64) * sizeof(float));
 }
 
+// Stored-gamma form (see DenseArgs::Gam): bf16/fp16 MFMA shapes with dropout
+// whose mask is causal and / or a window only, with each (batch, head)'s
+// blocks addressable by 32-bit offsets.  (Measured on MI355X: with dropout the
+// recomputing dQ kernel also replays the Philox draws and the stored form
+// wins; without dropout the extra HBM traffic of writing and reading gamma
+// costs more than the recomputation it saves.)  Returns the blocks per
+// (batch, head), 0 if not eligible.
+static long long gam_eligible(attn_dtype dt, int n_q, int n_k, int d, int dv, const attn_mask_t* mask,
+                              const attn_dropout_t* drop, int* stride) {
+  if (dt == ATTN_F32 || !dense_mfma_supported(d, dv)) return 0;
+  if (!drop || !(drop->rate > 0.f)) return 0;
+  MaskArgs m;
+  std::memset(&m, 0, sizeof(m));
+  if (mask) {
+    if (mask->block_mask || mask->dense_mask || mask->lengths || mask->starts) return 0;
+    m.causal = mask->causal != 0;
+    m.window = mask->window;
+  }
+  const long long per = gam_blocks_per_bh(m, n_q, n_k, *stride);
+  if (per <= 0 || per * kGamBlockBytes >= (1ll << 31)) return 0;
+  return per;
+}
+
+size_t attn_bwd_workspace_size_fast(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
+                                    const attn_mask_t* mask, const attn_dropout_t* dropout) {
+  const size_t base = attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv);
+  if (base == 0 || bad_dims({H_kv, n_k, d, dv})) return base;
+  int stride = 0;
+  const long long per = gam_eligible(dt, n_q, n_k, d, dv, mask, dropout, &stride);
+  if (per == 0) return base;
+  return round_up(base) + (size_t)B * H * (size_t)per * kGamBlockBytes;
+}
+
 static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
                               int dv, const void* Q, const void* K, const void* V, const void* Y,
                               const float* LSE, const void* G, const attn_mask_t* mask, float scale,
@@ -208,6 +241,12 @@ static attn_status bwd_common(int phases, attn_dtype dt, int B, int H, int H_kv,
   a.Q = Q; a.K = K; a.V = V; a.Y = Y; a.LSE = (float*)LSE; a.G = G;
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.Dws = (float*)workspace;
   a.Lws = (float*)((char*)workspace + round_up(((size_t)B * H * n_q + 64) * sizeof(float)));
+  // the stored-gamma form when the workspace holds its blocks
+  if (workspace_bytes >= attn_bwd_workspace_size_fast(dt, B, H, H_kv, n_q, n_k, d, dv, mask, dropout) &&
+      gam_eligible(dt, n_q, n_k, d, dv, mask, dropout, &a.gam_stride) > 0) {
+    a.gam_per_bh = gam_eligible(dt, n_q, n_k, d, dv, mask, dropout, &a.gam_stride);
+    a.Gam = (char*)workspace + round_up(need);
+  }
   const int rc = dt == ATTN_F32 ? launch_dense_bwd_f32(a, stream, phases)
                                 : launch_dense_bwd(a, dt == ATTN_BF16 ? Dt::BF16 : Dt::F16, stream, phases);
   if (rc != 0) return ATTN_ERR_HIP;
@@ -266,8 +305,9 @@ attn_status attn_bwd_noalloc(attn_dtype dt, int B, int H, int H_kv, int n_q, int
   void* ws = nullptr;
   st = noalloc_scratch(&ws);
   if (st != ATTN_OK) return st;
+  // exactly the minimal workspace: the recomputing form, whatever the mask
   return bwd_common(7, dt, B, H, H_kv, n_q, n_k, d, dv, Q, K, V, Y, LSE, G, mask, scale, block_b, dropout, dQ, dK,
-                    dV, ws, kNoAllocScratchBytes, stream);
+                    dV, ws, attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv), stream);
 }
 
 attn_status attn_bwd_phase(int phases, attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,

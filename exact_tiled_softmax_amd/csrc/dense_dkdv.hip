@@ -150,6 +150,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
   const int nq = a.nq, nk = a.nk;
   const int BG = a.B * a.Hkv, grp = a.H / a.Hkv;
   const float sl2 = a.scale_log2;
+  // stored gamma (see DenseArgs::Gam): with dropout, causal / window masks only
+  constexpr bool kGam = MK == kArith && DROP;
+  const bool gam_on = kGam && a.Gam != nullptr;
   const RowOps32<ROWB> rops(lane);
   const TrOps32<ROWB> tops(lane);
   const TileCopy<BQ, D, 4> tcopy(wave, lane);
@@ -170,6 +173,29 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
     // active extents and row lower bounds of this batch
     const Layout lay = layout_of<MK>(a.mask, b, nq, nk);
     const int nqa = lay.len, nka = lay.nka;
+    // Stored gamma^T (causal / window masks only): this wave's 32 keys are
+    // rows 32 (wave & 1) .. + 31 of key tile k0 / 64 + wave / 2, and a step's
+    // 64 queries fill columns (qb0 & 64) .. + 63 of query tile qb0 / 128.  A
+    // block is stored as 16 register images of 1 KiB (one store instruction
+    // each, lane l at byte 16 l): image (qb0 & 64) / 8 + 4 (wave & 1) + 2 mq + u
+    // holds, in lane 32 h + r, the 16-byte chunk 4 mq + 2 h + u of the step's
+    // columns of row 32 (wave & 1) + r, i.e. columns 32 mq + 16 h + 8 u .. + 7
+    // (the dQ kernel's tile copy gathers the chunks back into rows).
+    const int gam_jt = (k0 >> 6) + (wave >> 1);
+    const uint32_t gam_voff = (uint32_t)(16 * lane);
+    // the wave's block of step (qb0, bh) in the dQ kernel's tile set: resource
+    // over the (batch, head)'s blocks and the byte offset of its columns
+    auto gam_target = [&](int qb0, int bh, __amdgpu_buffer_rsrc_t& rs, uint32_t& soff) __attribute__((always_inline)) {
+      int lo, hi;
+      const int qt = qb0 >> 7;
+      gam_range(a.mask, qt, nq, nk, lo, hi);
+      if (gam_jt < lo || gam_jt > hi) return false;
+      const size_t per = (size_t)a.gam_per_bh * kGamBlockBytes;
+      rs = make_rsrc((const char*)a.Gam + (size_t)bh * per, (uint32_t)per);
+      soff = (uint32_t)(gam_block(a.gam_stride, qt, gam_jt, lo) * kGamBlockBytes) +
+             (uint32_t)(((qb0 & 64) / 8 + 4 * (wave & 1)) * 1024);
+      return true;
+    };
 
     const uint16_t* Kp = (const uint16_t*)a.K + (size_t)bg * nk * D;
     const uint16_t* Vp = (const uint16_t*)a.V + (size_t)bg * nk * D;
@@ -197,6 +223,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
     int qt_lo = 0, qt_hi = nqa > 0 ? (nqa - 1) / BQ : -1;
     if (a.mask.causal) qt_lo = k0 / BQ;
     if (a.mask.window > 0) qt_hi = min(qt_hi, (klast + a.mask.window - 1) / BQ);
+    // with stored gamma, whole 128-query tiles: the dQ kernel reads both halves
+    if (gam_on) qt_hi = min(nqa > 0 ? (nqa - 1) / BQ : -1, qt_hi | 1);
     const int n_qt = qt_hi - qt_lo + 1;
     const int total = (n_qt > 0) ? n_qt * grp : 0;
     // step classes of the per-element mask kinds, 64 steps at a time (row
@@ -377,6 +405,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
       int qb0;
       step_rows(st, lo, qb0);
       const int lane_bh = (int)(lo / nq);
+      __amdgpu_buffer_rsrc_t grs = make_rsrc(a.Gam, 0u);
+      uint32_t gsoff = 0;
+      const bool gst = gam_on && gam_target(qb0, lane_bh, grs, gsoff);
       copy_lse(sn, Next{});
       f32x16 sc[BQ / 32], dp[BQ / 32];
       Weights w[BQ / 32];
@@ -416,6 +447,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
           constexpr int kh = u / (2 * MD), md = (u % (2 * MD)) / 2;
           if constexpr (u & 1) dk[md] = E::mfma32(op, pack_op(w[mq].gw, kh), dk[md]);
           else dv[md] = E::mfma32(op, pack_op(w[mq].pw, kh), dv[md]);
+          // stored gamma: the block's gamma (complete before B(mq)) to its image
+          if constexpr (kGam && u < 2) {
+            if (gst)
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  u32x4{w[mq].gw[4 * u], w[mq].gw[4 * u + 1], w[mq].gw[4 * u + 2], w[mq].gw[4 * u + 3]}, grs,
+                  gam_voff, gsoff + (2 * mq + u) * 1024, 0);
+          }
         }
         // copies of the next step in the plan's copy groups
         if constexpr (Plan::copies[gi]) {
@@ -440,11 +478,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
         ETS_FENCE();
       });
     };
-    auto empty_step = [&](auto stg, int sn) __attribute__((always_inline)) {
+    auto empty_step = [&](auto stg, int st, int sn) __attribute__((always_inline)) {
       typedef std::integral_constant<int, 1 - decltype(stg)::value> Next;
       copy_lse(sn, Next{});
 #pragma unroll
       for (int u = 0; u < NCOPY; ++u) copy_one(sn, Next{}, u);
+      if (gam_on) {  // no allowed pair: a zero block part where the dQ kernel reads one
+        size_t lo;
+        int qb0;
+        step_rows(st, lo, qb0);
+        __amdgpu_buffer_rsrc_t grs = make_rsrc(a.Gam, 0u);
+        uint32_t gsoff = 0;
+        if (gam_target(qb0, (int)(lo / nq), grs, gsoff)) {
+          const u32x4 z = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int mq = 0; mq < BQ / 32; ++mq)  // the wave's four images
+#pragma unroll
+            for (int u = 0; u < 2; ++u) __builtin_amdgcn_raw_buffer_store_b128(z, grs, gam_voff, gsoff + (2 * mq + u) * 1024, 0);
+        }
+      }
     };
     auto finish = [&]() __attribute__((always_inline)) {
       wait_vm();
@@ -476,7 +528,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
           step(stg, st, sn, BodyTag<kPartIv>{}, false);
         }
       }
-      else empty_step(stg, sn);
+      else empty_step(stg, st, sn);
       finish();
     };
 

@@ -389,6 +389,142 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
   }
 }
 
+// --------------------------------------------------------------- dQ, stored
+// dQ from the gamma^T tiles the dK/dV kernel stored (causal / window masks):
+// dQ_i = c sum_j gamma_ij K_j with no recomputation.  A workgroup owns 128
+// query rows (32 per wave) of one (batch, head) and streams, per 64-key tile,
+// the K rows and the gamma^T block through a two-stage LDS ring; both
+// operands of dQ^T += K^T gamma^T are LDS transpose reads of row-major
+// [key][column] tiles, so their key orders agree.  Lane l of wave w
+// accumulates block column 32 w + l, i.e. query 32 w + (8 g + 4 h + r) for
+// l = 16 h + 4 g + r (the column order of the stored blocks).
+template <class E, int D>
+__global__ __launch_bounds__(256, 2) void dense_bwd_dq_stored_kernel(const DenseArgs a, int n_qtiles) {
+  constexpr int BK = 64;
+  constexpr int MD = D / 32;
+  constexpr int KROWB = D * 2, GROWB = 256;
+  typedef typename E::vec8 vec8;
+  typedef std::integral_constant<int, 0> Stage0;
+  typedef std::integral_constant<int, 1> Stage1;
+
+  __shared__ __attribute__((aligned(16))) char ldsK0[BK * KROWB], ldsG0[BK * GROWB], ldsK1[BK * KROWB],
+      ldsG1[BK * GROWB];
+  auto kbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsK0;
+    else return (char ETS_LDS*)ldsK1;
+  };
+  auto gbuf = [&](auto st) __attribute__((always_inline)) {
+    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsG0;
+    else return (char ETS_LDS*)ldsG1;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h32 = lane >> 5, l32 = lane & 31;
+  const int nq = a.nq, nk = a.nk;
+  const int BH = a.B * a.H;
+  const TrOps32<KROWB> ktops(lane);
+  // transpose-read offsets of this wave's 32 gamma^T columns: lane i of a
+  // 16-lane group addresses rows 4 h + i / 4 (and 8 + 4 h + i / 4) of a
+  // 16-row group at column 32 wave + 16 g + 4 (i % 4) (as TrOps32 does for a
+  // fixed column block; the swizzle depends on the row modulo 16 only)
+  int gt[2];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+    gt[sec] = toff<GROWB>(4 * h32 + 8 * sec + ((lane & 15) >> 2), 32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto gread = [&](const char ETS_LDS* base, int R) __attribute__((always_inline)) {
+    const s16x4 x = lds_tr4(base, gt[0] + R * GROWB), y = lds_tr4(base, gt[1] + R * GROWB);
+    const s16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(u32x4, v);
+  };
+  const TileCopy<BK, D, 4> kcopy(wave, lane);
+  // gamma^T tile copy: the LDS positions of a TileCopy<64, 128, 4> (instruction
+  // u of this wave fills chunk position 64 (4 wave + u) + lane with logical
+  // chunk c of row r), each fetched from where the dK/dV kernel stored it:
+  // image (c / 8) 8 + (r / 32) 4 + ((c / 4) % 2) 2 + c % 2, lane 32 ((c / 2) % 2) + r % 32
+  int goff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = wave * 16 + u * 4 + (lane >> 4), c = phys_chunk<GROWB>(r, lane & 15);
+    goff[u] = ((c >> 3) * 8 + (r >> 5) * 4 + ((c >> 2) & 1) * 2 + (c & 1)) * 1024 + (32 * ((c >> 1) & 1) + (r & 31)) * 16;
+  }
+  // this lane's query within the workgroup's 128 rows
+  const int qlane = 32 * wave + 8 * ((l32 & 15) >> 2) + 4 * (l32 >> 4) + (l32 & 3);
+  const size_t per = (size_t)a.gam_per_bh * kGamBlockBytes;
+
+  const int G = (int)gridDim.x, n_items = n_qtiles * BH;
+  for (int r = 0; r * G < n_items; ++r) {
+    const int item = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (item >= n_items) continue;
+    const int qt = n_qtiles - 1 - item / BH;  // most key tiles first
+    const int bh = item % BH;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.Hkv);
+    int lo, hi;
+    gam_range(a.mask, qt, nq, nk, lo, hi);
+    const __amdgpu_buffer_rsrc_t Krs =
+        make_rsrc((const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D, (uint32_t)nk * D * 2);
+    const __amdgpu_buffer_rsrc_t Grs = make_rsrc((const char*)a.Gam + (size_t)bh * per, (uint32_t)per);
+    const int blk0 = (int)gam_block(a.gam_stride, qt, 0, lo);  // block of key tile 0
+
+    f32x16 dq[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) dq[md][r2] = 0.f;
+
+    auto copy = [&](int jt, auto st) __attribute__((always_inline)) {
+      kcopy.issue(kbuf(st), Krs, jt * BK, nk - 1);
+      const int boff = (blk0 + jt) * kGamBlockBytes;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(Grs, (void ETS_LDS*)(gbuf(st) + (4 * wave + u) * 1024), 16, goff[u],
+                                                 boff, 0, 0);
+    };
+    auto tile = [&](auto st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const vec8 gop = as_vec8<E>(gread(gbuf(st), 32 * mb + 16 * kh));
+#pragma unroll
+          for (int md = 0; md < MD; ++md)
+            dq[md] = E::mfma32(as_vec8<E>(ktops.read(kbuf(st), 32 * mb + 16 * kh, md)), gop, dq[md]);
+        }
+    };
+    auto finish = [&]() __attribute__((always_inline)) {
+      wait_vm();
+      __syncthreads();
+    };
+    if (lo <= hi) copy(lo, Stage0{});
+    finish();
+    for (int jt = lo; jt <= hi; jt += 2) {
+      if (jt + 1 <= hi) copy(jt + 1, Stage1{});
+      tile(Stage0{});
+      finish();
+      if (jt + 1 > hi) break;
+      if (jt + 2 <= hi) copy(jt + 2, Stage0{});
+      tile(Stage1{});
+      finish();
+    }
+
+    const int qi = qt * 128 + qlane;
+    if (qi < nq) {
+      uint16_t* dQp = (uint16_t*)a.dQ + (size_t)bh * nq * D + (size_t)qi * D;
+      const float c = a.scale;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * md + 8 * g4 + 4 * h32;
+          u32x2 wv;
+          wv[0] = E::pack2(dq[md][4 * g4] * c, dq[md][4 * g4 + 1] * c);
+          wv[1] = E::pack2(dq[md][4 * g4 + 2] * c, dq[md][4 * g4 + 3] * c);
+          *(u32x2*)(dQp + col) = wv;
+        }
+    }
+  }
+}
+
 template <class E, int D, int MK, bool DROP>
 static int launch_dq_k(const DenseArgs& a, hipStream_t st) {
   const int n_qtiles = (a.nq + 127) / 128;
@@ -402,6 +538,14 @@ static int launch_dq_k(const DenseArgs& a, hipStream_t st) {
 template <class E, int D>
 static int launch_dq(const DenseArgs& a, hipStream_t st) {
   const int mk = mask_kind(a.mask);
+  if (a.Gam && mk == kArith) {
+    const int n_qtiles = (a.nq + 127) / 128;
+    const int n_items = n_qtiles * a.B * a.H;
+    int slots = 0;
+    ETS_TRY(resident_slots(dense_bwd_dq_stored_kernel<E, D>, 256, &slots));
+    ETS_TRY(launch((dense_bwd_dq_stored_kernel<E, D>), dim3(min(n_items, slots)), dim3(256), 0, st, a, n_qtiles));
+    return 0;
+  }
   if (a.drop.enabled) {
     if (mk == kArith) return launch_dq_k<E, D, kArith, true>(a, st);
     if (mk == kLayout) return launch_dq_k<E, D, kLayout, true>(a, st);

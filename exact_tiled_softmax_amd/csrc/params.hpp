@@ -1,6 +1,8 @@
 // Launch parameters shared by the C-ABI layer (abi.cpp) and the HIP kernels.
 // Internal to the library: nothing here is part of the public ABI.
 #pragma once
+#include <hip/hip_runtime.h>
+
 #include <cstddef>
 #include <cstdint>
 
@@ -43,7 +45,52 @@ struct DenseArgs {
   int block_b;                        // key-block size (fp32 path)
   MaskArgs mask;
   DropArgs drop;
+  // Stored-gamma form of the backward (bf16/fp16, causal and window masks
+  // only): the dK/dV kernel also writes every gamma^T tile it forms into Gam,
+  // and the dQ kernel reads them back instead of recomputing S and dP.  Null:
+  // the dQ kernel recomputes (the layout is in gam_range / gam_block below).
+  void* Gam;
+  int gam_stride;                     // blocks per 128-query tile; 0 = causal triangle
+  long long gam_per_bh;               // blocks per (batch, query head)
 };
+
+// Stored gamma^T blocks.  One block holds gamma^T of 64 keys x 128 queries
+// (rows of 128 16-bit values, 16 KiB), for 64-key tile jt and 128-query tile
+// qt of one (batch, query head).  Within a 32-query group the columns are
+// permuted: column 16h + 4g + r holds query 8g + 4h + r, the order in which a
+// dK/dV lane holds its 16 rows of a 32-row block.  gam_range gives the key
+// tiles [lo, hi] a query tile sees under a causal / window mask (the tiles
+// the dQ kernel visits; hi < lo when none), and gam_block the block index of
+// (qt, jt) within its (batch, head): tiles of one query tile are consecutive,
+// query tiles follow at a fixed stride, or, for causal masks without a
+// window, at the triangle offsets qt (qt + 1) (query tile qt sees at most
+// 2 qt + 2 key tiles).
+constexpr int kGamBlockBytes = 64 * 128 * 2;
+__host__ __device__ inline void gam_range(const MaskArgs& m, int qt, int nq, int nk, int& lo, int& hi) {
+  const int q0 = qt * 128, qlast = (q0 + 128 < nq ? q0 + 128 : nq) - 1;
+  lo = 0;
+  hi = (nk - 1) / 64;
+  if (nk < 1 || q0 >= nq) hi = -1;
+  if (m.causal && qlast / 64 < hi) hi = qlast / 64;
+  if (m.window > 0) {
+    const int l = (q0 - m.window + 1) / 64;
+    lo = l > 0 ? l : 0;
+  }
+}
+__host__ __device__ inline long long gam_block(int stride, int qt, int jt, int lo) {
+  return (stride ? (long long)qt * stride : (long long)qt * (qt + 1)) + (jt - lo);
+}
+// Blocks per (batch, head) and the stride for a causal / window mask
+__host__ __device__ inline long long gam_blocks_per_bh(const MaskArgs& m, int nq, int nk, int& stride) {
+  const int nqt = (nq + 127) / 128, nkt = (nk + 63) / 64;
+  if (m.causal && m.window <= 0) {
+    stride = 0;
+    return (long long)nqt * (nqt + 1);
+  }
+  stride = nkt;
+  if (m.causal && m.window > 0 && (m.window + 126) / 64 + 2 < nkt) stride = (m.window + 126) / 64 + 2;
+  return (long long)nqt * stride;
+}
 
 struct SparseArgs {
   const void* Q; const void* KV;

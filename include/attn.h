@@ -155,6 +155,26 @@ size_t attn_bwd_workspace_size(attn_dtype dt, int B, int H, int H_kv, int n_q, i
                                int dv);
 
 /*
+ * Bytes of workspace with which attn_bwd takes its stored-gamma form for this
+ * mask and dropout, or attn_bwd_workspace_size() when the call has none.  The
+ * form exists for bf16/fp16 with dropout (rate > 0) and a causal and / or
+ * window mask only (no block mask, dense mask, lengths or starts): the dK/dV
+ * kernel, which forms every gamma_ij = p_ij (kappa_ij G_i . V_j - D_i) of the
+ * reverse pass ([P1] paragraphs 4-6) anyway, also writes them (rounded to the
+ * input dtype, as its own products use them) to the workspace, and the dQ
+ * product dQ_i = c sum_j gamma_ij K_j reads them back instead of recomputing
+ * s_ij, G_i . V_j and the dropout draws.  The extra space is 16 KiB per
+ * 64-key x 128-query tile that the mask reaches, per (batch, query head):
+ * B H ceil(n/128) (ceil(n/128) + 1) tiles for a causal mask, e.g. 1.09 GB for
+ * B = 1, H = 16, n = 8192.  attn_bwd (and attn_bwd_phase) take this form
+ * whenever the call has it and workspace_bytes is at least this size; the
+ * gradients agree with the recomputing form to rounding.  (Without dropout
+ * the form is slower than the recomputation on MI355X, so it is not offered.)
+ */
+size_t attn_bwd_workspace_size_fast(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d,
+                                    int dv, const attn_mask_t* mask, const attn_dropout_t* dropout);
+
+/*
  * attn_bwd -- block-recomputed reverse pass ([P1] paragraphs 4-6, [P3]
  * "Reconstruct probabilities when a gradient needs them"): the exact gradient
  * of Phi = sum_i sum_a G_ia Y_ia,
@@ -184,7 +204,10 @@ attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, in
  * streams once the prepass is done) or time them one by one.  `phases` is a
  * bit set: 1 = the prepass D_i = G_i . Y_i into the workspace, 2 = dK and dV,
  * 4 = dQ; phases 2 and 4 read the D_i a completed phase 1 left in the same
- * workspace and are independent of each other.  attn_bwd is phases = 7.
+ * workspace and are independent of each other, except in the stored-gamma
+ * form (a workspace of attn_bwd_workspace_size_fast() bytes), where phase 4
+ * reads the gamma tiles phase 2 wrote and must follow it.  attn_bwd is
+ * phases = 7.
  * Pointers a selected phase does not use may be NULL (phase 1 reads Y and G;
  * phases 2 and 4 read Q, K, V, LSE and G; phase 2 writes dK, dV; phase 4
  * writes dQ).  Other arguments and errors as attn_bwd; phases outside 1..7

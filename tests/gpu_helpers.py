@@ -62,8 +62,11 @@ def mask_arg(causal=False, window=0, block_mask=None, block_q=64, block_k=64, de
     return d
 
 
-def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=True):
-    """Run attn_fwd (and attn_bwd) on storage arrays; return float64 results."""
+def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=True, ws_form="fast"):
+    """Run attn_fwd (and attn_bwd) on storage arrays; return float64 results.
+    ws_form "fast": a workspace of attn_bwd_workspace_size_fast bytes (the
+    stored-gamma backward where the call has one: dropout with a causal /
+    window mask), "min": the minimal one (the dQ kernel recomputes)."""
     import exact_tiled_softmax_amd as ets
     torch = torch_cuda()
     B, H, n_q, d = Q.shape
@@ -77,8 +80,13 @@ def dense_run(dtype, Q, K, V, G, mask, scale, block_b=0, dropout=None, backward=
     if backward:
         dg = to_dev(G, dtype)
         dQ, dK, dV = empty(Q.shape, dtype), empty(K.shape, dtype), empty(V.shape, dtype)
-        ws_bytes = ets.attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        if ws_form == "fast":
+            ws_bytes = ets.attn_bwd_workspace_size_fast(dt, B, H, H_kv, n_q, n_k, d, dv, mask, dropout)
+        else:
+            ws_bytes = ets.attn_bwd_workspace_size(dt, B, H, H_kv, n_q, n_k, d, dv)
+        # all-ones bytes (NaN as bf16 / fp16 / fp32): a workspace entry read
+        # before it is written turns the gradients into NaN
+        ws = torch.full((ws_bytes,), 255, dtype=torch.uint8, device="cuda")
         ets.attn_bwd(dt, B, H, H_kv, n_q, n_k, d, dv, dq, dk, dvv, Y, LSE, dg, mask, scale, block_b,
                      dropout, dQ, dK, dV, ws, ws_bytes)
         out.update(dQ=dQ, dK=dK, dV=dV)

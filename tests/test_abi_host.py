@@ -50,6 +50,38 @@ def test_workspace_sizes():
     assert ets.attn_sparse_bwd_det_workspace_size(4096, 64, 16384, 576, 512, 2048) == 2 * 4096 * 64 * 4 + 16384 * 576 * 8
 
 
+def test_stored_gamma_workspace_sizes():
+    # 16 KiB per (64-key, 128-query) tile a causal / window mask reaches, per
+    # (batch, head), with dropout: n = 8192 causal has 64 query tiles, 64 * 65
+    # tile slots; n = 2048, 16 * 17
+    import exact_tiled_softmax_amd as ets
+    drop = (0.1, 0)
+    base = ets.attn_bwd_workspace_size(ets.ATTN_BF16, 1, 16, 16, 8192, 8192, 128, 128)
+    fast = ets.attn_bwd_workspace_size_fast(ets.ATTN_BF16, 1, 16, 16, 8192, 8192, 128, 128, {"causal": 1}, drop)
+    assert fast == base + 16 * 64 * 65 * 16384
+    base = ets.attn_bwd_workspace_size(ets.ATTN_BF16, 4, 16, 16, 2048, 2048, 128, 128)
+    fast = ets.attn_bwd_workspace_size_fast(ets.ATTN_BF16, 4, 16, 16, 2048, 2048, 128, 128, {"causal": 1}, drop)
+    assert fast == base + 4 * 16 * 16 * 17 * 16384
+    # causal + 256-key window: at most (256 + 126) // 64 + 2 = 7 key tiles per query tile
+    fast = ets.attn_bwd_workspace_size_fast(ets.ATTN_F16, 2, 32, 32, 4096, 4096, 64, 64,
+                                            {"causal": 1, "window": 256}, drop)
+    assert fast == ets.attn_bwd_workspace_size(ets.ATTN_F16, 2, 32, 32, 4096, 4096, 64, 64) + 64 * 32 * 7 * 16384
+    # no mask, n_q != n_k: every key tile of every query tile
+    fast = ets.attn_bwd_workspace_size_fast(ets.ATTN_BF16, 1, 2, 2, 150, 270, 64, 64, None, drop)
+    assert fast == ets.attn_bwd_workspace_size(ets.ATTN_BF16, 1, 2, 2, 150, 270, 64, 64) + 2 * 2 * 5 * 16384
+    # no stored form: without dropout (or at rate 0), fp32, unsupported widths,
+    # block masks, layouts; and a (batch, head) whose tiles pass 2 GiB
+    for args, mask, dr in (((ets.ATTN_BF16, 1, 1, 1, 256, 256, 64, 64), {"causal": 1}, None),
+                           ((ets.ATTN_BF16, 1, 1, 1, 256, 256, 64, 64), {"causal": 1}, (0.0, 3)),
+                           ((ets.ATTN_F32, 1, 1, 1, 256, 256, 64, 64), {"causal": 1}, drop),
+                           ((ets.ATTN_BF16, 1, 1, 1, 256, 256, 96, 96), {"causal": 1}, drop),
+                           ((ets.ATTN_BF16, 1, 1, 1, 256, 256, 64, 64), {"causal": 1, "block_mask": P, "block_q": 64,
+                                                                          "block_k": 64}, drop),
+                           ((ets.ATTN_BF16, 1, 1, 1, 256, 256, 64, 64), {"causal": 1, "lengths": P}, drop),
+                           ((ets.ATTN_BF16, 1, 1, 1, 1 << 16, 1 << 16, 64, 64), {"causal": 1}, drop)):
+        assert ets.attn_bwd_workspace_size_fast(*args, mask, dr) == ets.attn_bwd_workspace_size(*args)
+
+
 P = 0x10000  # a dummy aligned address: never dereferenced, every call fails validation
 
 

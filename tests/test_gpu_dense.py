@@ -317,26 +317,31 @@ def test_lds_probe_reads_what_it_wrote():
     assert np.all(got == acc)
 
 
+@pytest.mark.parametrize("form", ["min", "fast"])
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
-def test_backward_phases_reproduce_attn_bwd(dtype, d):
+def test_backward_phases_reproduce_attn_bwd(dtype, d, form):
     # attn_bwd_phase(1), (2), (4) in turn run the same kernels on the same
-    # workspace as attn_bwd, so the gradients agree bit for bit
+    # workspace as attn_bwd, so the gradients agree bit for bit (in the
+    # stored-gamma form phase 4 reads the tiles phase 2 wrote)
     import exact_tiled_softmax_amd as ets
     torch = gh.torch_cuda()
     n = 333
     a = _inputs(1, 4, 2, n, d, d, dtype, 77)
     c = 1.0 / math.sqrt(d)
     mask = gh.mask_arg(causal=True, window=200)
-    r = gh.dense_run(dtype, a["Q"], a["K"], a["V"], a["G"], mask, c)
+    drop = (0.15, 99) if form == "fast" else None  # the stored-gamma form needs dropout
+    r = gh.dense_run(dtype, a["Q"], a["K"], a["V"], a["G"], mask, c, dropout=drop, ws_form=form)
     dev = r["_dev"]
     dt = gh.DT[dtype]
     shape = (dt, 1, 4, 2, n, n, d, d)
     q, k, v, g = (gh.to_dev(a[x], dtype) for x in ("Q", "K", "V", "G"))
     dQ, dK, dV = gh.empty(a["Q"].shape, dtype), gh.empty(a["K"].shape, dtype), gh.empty(a["V"].shape, dtype)
-    nb = ets.attn_bwd_workspace_size(*shape)
+    nb = ets.attn_bwd_workspace_size(*shape) if form == "min" else ets.attn_bwd_workspace_size_fast(*shape, mask,
+                                                                                                  drop)
+    assert form == "min" or nb > ets.attn_bwd_workspace_size(*shape)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     for ph in (1, 2, 4):
-        ets.attn_bwd_phase(ph, *shape, q, k, v, dev["Y"], dev["LSE"], g, mask, c, 0, None, dQ, dK, dV, ws, nb)
+        ets.attn_bwd_phase(ph, *shape, q, k, v, dev["Y"], dev["LSE"], g, mask, c, 0, drop, dQ, dK, dV, ws, nb)
     torch.cuda.synchronize()
     for name, t in (("dQ", dQ), ("dK", dK), ("dV", dV)):
         assert np.array_equal(gh.from_dev(t, dtype), r[name]), name

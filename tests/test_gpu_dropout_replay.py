@@ -14,7 +14,9 @@ With Q = 0 every score is 0, so p_ij = 1 / |A_i| on the causal set A_i =
                      G_i = e_{i-rd} for rows i of block r (0 elsewhere):
                        Y_i[c]  = p_i kappa xi_{i, rd+c}          (rd + c <= i)
                        dV_j[c] = p_i kappa xi_{i, j}, i = rd + c (j <= i)
-  dQ run:            K_j = e_{j-rd} for keys of block r, V_j = G_i = e_0:
+  dQ run (twice: with the minimal workspace the dQ kernel replays xi itself;
+  with the larger one it reads the gamma tiles the dK/dV kernel stored):
+                     K_j = e_{j-rd} for keys of block r, V_j = G_i = e_0:
                        dQ_i[c] = scale p_i (kappa xi_{i, rd+c} - D_i),
                        D_i = G_i . Y_i = Y_i[0]
 so xi is nonzero-ness of Y and dV, and the nearer of the two candidate values
@@ -42,6 +44,7 @@ def _decode(dtype, d, n, rate, seed, H=2):
     xi_y = np.zeros((H, n, n), np.int8) - 1   # -1: not decoded
     xi_dv = np.zeros((H, n, n), np.int8) - 1
     xi_dq = np.zeros((H, n, n), np.int8) - 1
+    xi_dqs = np.zeros((H, n, n), np.int8) - 1
     mask = gh.mask_arg(causal=True)
     zeros_qk = np.zeros((B, H, n, d))
     p = 1.0 / np.arange(1, n + 1)
@@ -65,20 +68,24 @@ def _decode(dtype, d, n, rate, seed, H=2):
         # dQ run
         e0 = np.zeros((B, H, n, d))
         e0[..., 0] = 1.0
-        res = gh.dense_run(dtype, _st(zeros_qk, dtype), _st(onehot, dtype), _st(e0, dtype), _st(e0, dtype),
-                           mask, 1.0, dropout=(rate, seed))
-        for h in range(H):
-            Y, dQ = res["Y"][0, h], res["dQ"][0, h]
-            D = Y[:, 0]
-            for cc, j in zip(c, blk):
-                rows = np.arange(j, n)
-                kept = p[rows] * (kappa - D[rows])
-                dropped = -p[rows] * D[rows]
-                got = dQ[rows, cc]
-                xi_dq[h, rows, j] = np.abs(got - kept) < np.abs(got - dropped)
+        for form, xi_out in (("min", xi_dq), ("fast", xi_dqs)):
+            res = gh.dense_run(dtype, _st(zeros_qk, dtype), _st(onehot, dtype), _st(e0, dtype), _st(e0, dtype),
+                               mask, 1.0, dropout=(rate, seed), ws_form=form)
+            for h in range(H):
+                Y, dQ = res["Y"][0, h], res["dQ"][0, h]
+                D = Y[:, 0]
+                for cc, j in zip(c, blk):
+                    rows = np.arange(j, n)
+                    kept = p[rows] * (kappa - D[rows])
+                    dropped = -p[rows] * D[rows]
+                    got = dQ[rows, cc]
+                    xi_out[h, rows, j] = np.abs(got - kept) < np.abs(got - dropped)
     want = np.stack([philox.keep_mask(seed, float(np.float32(rate)), h, np.arange(n), np.arange(n))
                      for h in range(H)]).astype(np.int8)
-    for name, xi in (("forward", xi_y), ("dK/dV", xi_dv), ("dQ", xi_dq)):
+    checks = [("forward", xi_y), ("dK/dV", xi_dv), ("dQ", xi_dq)]
+    if dtype != "f32":  # the fp32 path has no stored-gamma form
+        checks.append(("dQ from stored gamma", xi_dqs))
+    for name, xi in checks:
         assert np.all(xi[:, tri] >= 0), f"{name}: pairs left undecoded"
         bad = np.argwhere((xi != want) & tri[None])
         assert bad.size == 0, f"{name}: {len(bad)} xi bits differ, first (head, row, key) {bad[:5].tolist()}"
