@@ -173,16 +173,22 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       const int u = t - 2 * NA, mb = u / NB, kh = (u % NB) / MD, md = u % MD;
       return as_vec8<E>(tops.read(kbuf(st), 32 * mb + 16 * kh, md));
     };
-    // key interval of this lane's row for arithmetic masks: key base + c is
-    // allowed iff (unsigned)(c - lo) <= rng
-    auto arith_interval = [&](int base, int& lo, unsigned& rng) __attribute__((always_inline)) {
+    // allowed keys of this lane's row under the interval parts of the mask
+    // (causal, window, lengths, starts), fixed for the item: key j passes them
+    // iff (unsigned)(j - iv_lo) <= iv_rng.  Tiles on the interval body (every
+    // mask kind, a tile mask only where it is uniform over the wave's tile)
+    // apply just this test.
+    int iv_lo = 1 << 30;
+    unsigned iv_rng = 0u;
+    {
       int jlo = max(0, st_i), jhi = nka - 1;
       if (a.mask.causal) jhi = min(jhi, qi);
       if (a.mask.window > 0) jlo = max(jlo, qi - a.mask.window + 1);
-      const bool any = qi < nqa && jlo <= jhi;
-      lo = any ? jlo - base : (1 << 24);
-      rng = any ? (unsigned)(jhi - jlo) : 0u;
-    };
+      if (qi < nqa && jlo <= jhi) {
+        iv_lo = jlo;
+        iv_rng = (unsigned)(jhi - jlo);
+      }
+    }
     struct Gam {
       uint32_t gw[8];
       unsigned allow[4];
@@ -194,21 +200,9 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
       constexpr bool PART = decltype(part_tag)::value != kWhole;
       const int g4 = k / 2, half = k % 2;
       const int jj = key0 + 8 * g4 + 4 * h32;
-      if (half == 0) {
-        w.allow[g4] = 0xFu;
-        if constexpr (PART) {
-          if constexpr (decltype(part_tag)::value == kPartIv) {
-            int lo;
-            unsigned rng;
-            arith_interval(jj, lo, rng);
-            unsigned al = 0;
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) al |= ((unsigned)(r2 - lo) <= rng ? 1u : 0u) << r2;
-            w.allow[g4] = al;
-          } else {
-            w.allow[g4] = allowed4<MK>(a.mask, qi, jj, nqa, nka, cbm, lay.st);
-          }
-        }
+      constexpr bool IV = decltype(part_tag)::value == kPartIv;
+      if constexpr (PART && !IV) {
+        if (half == 0) w.allow[g4] = allowed4<MK>(a.mask, qi, jj, nqa, nka, cbm, lay.st);
       }
       float gm[2];
 #pragma unroll
@@ -217,7 +211,9 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
         const float pv = fast_exp2(fmaf(sc[4 * g4 + r2], sl2, -lse2));
         float dpv = dp[4 * g4 + r2];
         if constexpr (DROP) dpv = ((w.keep >> (8 * g4 + r2)) & 1u) ? dpv * a.drop.inv_keep : 0.f;
-        const bool al = !PART || ((w.allow[g4] >> r2) & 1u);
+        bool al = true;
+        if constexpr (IV) al = (unsigned)(jj + r2 - iv_lo) <= iv_rng;
+        else if constexpr (PART) al = (w.allow[g4] >> r2) & 1u;
         gm[e] = al ? pv * (dpv + ndval) : 0.f;
       }
       w.gw[2 * g4 + half] = E::pack2(gm[0], gm[1]);
