@@ -75,9 +75,12 @@ def host_cores_and_model():
     return int(cores), model
 
 
-def dense_algorithmic_bytes(w):
+def dense_algorithmic_bytes(w, gam_bytes=0):
     """Compulsory HBM bytes per launch of each dense kernel: every input read
-    once, every output written once (dtype-sized tensors, fp32 LSE / D rows)."""
+    once, every output written once (dtype-sized tensors, fp32 LSE / D rows).
+    With the stored-gamma backward (gam_bytes of gamma tiles), the dK/dV
+    kernel also writes the tiles and the dQ kernel reads K and the tiles and
+    writes dQ."""
     esz = 4 if w.dtype == "f32" else 2
     q = w.B * w.H * w.n * w.d * esz            # Q, dQ
     g = w.B * w.H * w.n * w.dv * esz           # G, Y
@@ -86,8 +89,23 @@ def dense_algorithmic_bytes(w):
     row = w.B * w.H * w.n * 4                  # one fp32 per query row (LSE, D, LSE2)
     return {"fwd": q + k + v + g + row,        # Q, K, V read; Y, LSE written
             "bwd_prep": 2 * g + row + 2 * row,  # G, Y, LSE read; D, LSE2 written
-            "bwd_dkdv": q + g + k + v + 2 * row + k + v,  # Q, G, K, V, LSE2, D read; dK, dV written
-            "bwd_dq": q + g + k + v + 2 * row + q}         # Q, G, K, V, LSE2, D read; dQ written
+            "bwd_dkdv": q + g + k + v + 2 * row + k + v + gam_bytes,  # Q, G, K, V, LSE2, D read; dK, dV (gamma) written
+            "bwd_dq": (k + gam_bytes + q) if gam_bytes else (q + g + k + v + 2 * row + q)}  # inputs read; dQ written
+
+
+def stored_gamma_bytes(w):
+    """Bytes of the gamma tiles the stored-gamma backward writes and reads:
+    16 KiB per (64-key, 128-query) tile that a causal / window mask reaches,
+    per (batch, head)."""
+    tiles = 0
+    for qt in range((w.n + 127) // 128):
+        q0 = qt * 128
+        hi = (w.n - 1) // 64
+        if w.causal:
+            hi = min(hi, (min(q0 + 128, w.n) - 1) // 64)
+        lo = max(0, int((q0 - w.window + 1) / 64)) if w.window > 0 else 0
+        tiles += max(0, hi - lo + 1)
+    return w.B * w.H * tiles * 64 * 128 * 2
 
 
 def sources_sha256(kernel):
@@ -337,7 +355,8 @@ def bench_dense(w, args):
     f_fwd, f_bwd = flops["fwd"], flops["bwd_dkdv"] + flops["bwd_dq"]
     peak = PEAK_TFLOPS[w.dtype]
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    nbytes = dense_algorithmic_bytes(w)
+    gam_bytes = stored_gamma_bytes(w) if ws_bytes > ets.attn_bwd_workspace_size(*shape) else 0
+    nbytes = dense_algorithmic_bytes(w, gam_bytes)
     kernels = {}
     for n in names:
         gbs = nbytes[n] / (kern_ms[n] * 1e-3) / 1e9
