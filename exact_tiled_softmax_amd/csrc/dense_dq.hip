@@ -386,32 +386,41 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_kernel(const DenseArgs a,
 }
 
 // --------------------------------------------------------------- dQ, stored
-// dQ from the gamma^T tiles the dK/dV kernel stored (causal / window masks):
-// dQ_i = c sum_j gamma_ij K_j with no recomputation.  A workgroup owns 128
-// query rows (32 per wave) of one (batch, head) and streams, per 64-key tile,
-// the K rows and the gamma^T block through a two-stage LDS ring; both
-// operands of dQ^T += K^T gamma^T are LDS transpose reads of row-major
-// [key][column] tiles, so their key orders agree.  Lane l of wave w
-// accumulates block column 32 w + l, i.e. query 32 w + (8 g + 4 h + r) for
-// l = 16 h + 4 g + r (the column order of the stored blocks).
+// dQ from the gamma^T tiles the dK/dV kernel stored (dropout with causal /
+// window masks): dQ_i = c sum_j gamma_ij K_j with no recomputation.  A
+// workgroup owns 128 query rows (32 per wave) of one (batch, head) and streams
+// half tiles of 32 keys -- their K rows and their half of the gamma^T block --
+// through a four-stage LDS ring, three half tiles ahead (the kernel is bound
+// by how many bytes it keeps in flight); both operands of
+// dQ^T += K^T gamma^T are LDS transpose reads of row-major [key][column]
+// tiles, so their key orders agree.  Lane l of wave w accumulates block
+// column 32 w + l, i.e. query 32 w + (8 g + 4 h + r) for l = 16 h + 4 g + r
+// (the column order of the stored blocks).
 template <class E, int D>
 __global__ __launch_bounds__(256, 2) void dense_bwd_dq_stored_kernel(const DenseArgs a, int n_qtiles) {
-  constexpr int BK = 64;
+  constexpr int BK = 32;  // keys per half tile
   constexpr int MD = D / 32;
-  constexpr int KROWB = D * 2, GROWB = 256;
+  constexpr int KROWB = D * 2, GROWB = 256, GSUBB = 128;
   typedef typename E::vec8 vec8;
-  typedef std::integral_constant<int, 0> Stage0;
-  typedef std::integral_constant<int, 1> Stage1;
+  constexpr int KPW = TileCopy<BK, D, 4>::PER_WAVE;
+  constexpr int NV = KPW + 2;  // copy instructions per wave per half tile
 
-  __shared__ __attribute__((aligned(16))) char ldsK0[BK * KROWB], ldsG0[BK * GROWB], ldsK1[BK * KROWB],
-      ldsG1[BK * GROWB];
+  // one array per (stage, tensor), so that every LDS access names its stage
+  __shared__ __attribute__((aligned(16))) char ldsK0[BK * KROWB], ldsK1[BK * KROWB], ldsK2[BK * KROWB],
+      ldsK3[BK * KROWB], ldsG0[BK * GROWB], ldsG1[BK * GROWB], ldsG2[BK * GROWB], ldsG3[BK * GROWB];
   auto kbuf = [&](auto st) __attribute__((always_inline)) {
-    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsK0;
-    else return (char ETS_LDS*)ldsK1;
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return (char ETS_LDS*)ldsK0;
+    else if constexpr (S == 1) return (char ETS_LDS*)ldsK1;
+    else if constexpr (S == 2) return (char ETS_LDS*)ldsK2;
+    else return (char ETS_LDS*)ldsK3;
   };
   auto gbuf = [&](auto st) __attribute__((always_inline)) {
-    if constexpr (decltype(st)::value == 0) return (char ETS_LDS*)ldsG0;
-    else return (char ETS_LDS*)ldsG1;
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return (char ETS_LDS*)ldsG0;
+    else if constexpr (S == 1) return (char ETS_LDS*)ldsG1;
+    else if constexpr (S == 2) return (char ETS_LDS*)ldsG2;
+    else return (char ETS_LDS*)ldsG3;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -420,29 +429,37 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_stored_kernel(const Dense
   const int nq = a.nq, nk = a.nk;
   const int BH = a.B * a.H;
   const TrOps32<KROWB> ktops(lane);
-  // transpose-read offsets of this wave's 32 gamma^T columns: lane i of a
-  // 16-lane group addresses rows 4 h + i / 4 (and 8 + 4 h + i / 4) of a
-  // 16-row group at column 32 wave + 16 g + 4 (i % 4) (as TrOps32 does for a
-  // fixed column block; the swizzle depends on the row modulo 16 only)
+  // The gamma^T half tile sits in LDS as two sub-tiles of 64 columns
+  // (32 rows of 128 bytes each, sub-tile s = columns 64 s .. 64 s + 63), so
+  // that each copy instruction fetches whole 128-byte runs of the stored
+  // images (below).  Transpose-read offsets of this wave's 32 columns (in
+  // sub-tile wave / 2): lane i of a 16-lane group addresses rows 4 h + i / 4
+  // (and 8 + 4 h + i / 4) of a 16-row group at column 32 (wave % 2) + 16 g +
+  // 4 (i % 4) (as TrOps32 does for a fixed column block; the swizzle depends on
+  // the row modulo 16 only).
   int gt[2];
 #pragma unroll
   for (int sec = 0; sec < 2; ++sec)
-    gt[sec] = toff<GROWB>(4 * h32 + 8 * sec + ((lane & 15) >> 2), 32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    gt[sec] = (wave >> 1) * (BK * GSUBB) +
+              toff<GSUBB>(4 * h32 + 8 * sec + ((lane & 15) >> 2), 32 * (wave & 1) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   auto gread = [&](const char ETS_LDS* base, int R) __attribute__((always_inline)) {
-    const s16x4 x = lds_tr4(base, gt[0] + R * GROWB), y = lds_tr4(base, gt[1] + R * GROWB);
+    const s16x4 x = lds_tr4(base, gt[0] + R * GSUBB), y = lds_tr4(base, gt[1] + R * GSUBB);
     const s16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(u32x4, v);
   };
   const TileCopy<BK, D, 4> kcopy(wave, lane);
-  // gamma^T tile copy: the LDS positions of a TileCopy<64, 128, 4> (instruction
-  // u of this wave fills chunk position 64 (4 wave + u) + lane with logical
-  // chunk c of row r), each fetched from where the dK/dV kernel stored it:
-  // image (c / 8) 8 + (r / 32) 4 + ((c / 4) % 2) 2 + c % 2, lane 32 ((c / 2) % 2) + r % 32
-  int goff[4];
+  // gamma^T half-tile copy: instruction k = 2 wave + u (u = 0, 1) fills the
+  // 64 chunk positions 64 (k % 4) .. of sub-tile s = k / 4, i.e. lane l fills
+  // row r = 8 (k % 4) + l / 8, logical chunk c = phys_chunk(r, l % 8) of the
+  // sub-tile; row 32 half + r, chunk 8 s + c of the block sits in image
+  // 8 s + 4 half + ((c / 4) % 2) 2 + c % 2, lane 32 ((c / 2) % 2) + r, so the
+  // instruction reads 8 runs of 8 consecutive 16-byte lanes (offsets below for
+  // half 0; half 1 is four images on)
+  int goff[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = wave * 16 + u * 4 + (lane >> 4), c = phys_chunk<GROWB>(r, lane & 15);
-    goff[u] = ((c >> 3) * 8 + (r >> 5) * 4 + ((c >> 2) & 1) * 2 + (c & 1)) * 1024 + (32 * ((c >> 1) & 1) + (r & 31)) * 16;
+  for (int u = 0; u < 2; ++u) {
+    const int k = 2 * wave + u, r = 8 * (k & 3) + (lane >> 3), c = phys_chunk<GSUBB>(r, lane & 7);
+    goff[u] = ((k >> 2) * 8 + ((c >> 2) & 1) * 2 + (c & 1)) * 1024 + (32 * ((c >> 1) & 1) + r) * 16;
   }
   // this lane's query within the workgroup's 128 rows
   const int qlane = 32 * wave + 8 * ((l32 & 15) >> 2) + 4 * (l32 >> 4) + (l32 & 3);
@@ -461,6 +478,7 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_stored_kernel(const Dense
         make_rsrc((const uint16_t*)a.K + (size_t)(b * a.Hkv + g) * nk * D, (uint32_t)nk * D * 2);
     const __amdgpu_buffer_rsrc_t Grs = make_rsrc((const char*)a.Gam + (size_t)bh * per, (uint32_t)per);
     const int blk0 = (int)gam_block(a.gam_stride, qt, 0, lo);  // block of key tile 0
+    const int t0 = 2 * lo, t1 = 2 * hi + 1;                    // half tiles t0 .. t1 (none when hi < lo)
 
     f32x16 dq[MD];
 #pragma unroll
@@ -468,40 +486,54 @@ __global__ __launch_bounds__(256, 2) void dense_bwd_dq_stored_kernel(const Dense
 #pragma unroll
       for (int r2 = 0; r2 < 16; ++r2) dq[md][r2] = 0.f;
 
-    auto copy = [&](int jt, auto st) __attribute__((always_inline)) {
-      kcopy.issue(kbuf(st), Krs, jt * BK, nk - 1);
-      const int boff = (blk0 + jt) * kGamBlockBytes;
+    // half tile t (keys 32 t .. 32 t + 31) into stage st: NV instructions per wave
+    auto copy = [&](int t, auto st) __attribute__((always_inline)) {
+      kcopy.issue(kbuf(st), Krs, t * BK, nk - 1);
+      const int boff = (blk0 + (t >> 1)) * kGamBlockBytes + (t & 1) * 4096;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(Grs, (void ETS_LDS*)(gbuf(st) + (4 * wave + u) * 1024), 16, goff[u],
-                                                 boff, 0, 0);
+      for (int u = 0; u < 2; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            Grs, (void ETS_LDS*)(gbuf(st) + (wave >> 1) * (BK * GSUBB) + ((2 * wave + u) & 3) * 1024), 16, goff[u],
+            boff, 0, 0);
     };
-    auto tile = [&](auto st) __attribute__((always_inline)) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const vec8 gop = as_vec8<E>(gread(gbuf(st), 32 * mb + 16 * kh));
-#pragma unroll
-          for (int md = 0; md < MD; ++md)
-            dq[md] = E::mfma32(as_vec8<E>(ktops.read(kbuf(st), 32 * mb + 16 * kh, md)), gop, dq[md]);
-        }
-    };
-    auto finish = [&]() __attribute__((always_inline)) {
-      wait_vm();
+    // half tile t on stage st: wait for its copies (the loads complete in
+    // order; the copies of up to two later half tiles may stay in flight),
+    // publish them, refill the stage read one step before with half tile
+    // t + 3, then the products
+    auto step = [&](auto st, int t) __attribute__((always_inline)) {
+      constexpr int S = decltype(st)::value;
+      if (t + 2 <= t1) wait_vm_n<2 * NV>();
+      else if (t + 1 <= t1) wait_vm_n<NV>();
+      else wait_vm();
       __syncthreads();
+      if (t + 3 <= t1) copy(t + 3, std::integral_constant<int, (S + 3) % 4>{});
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const vec8 gop = as_vec8<E>(gread(gbuf(st), 16 * kh));
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+          dq[md] = E::mfma32(as_vec8<E>(ktops.read(kbuf(st), 16 * kh, md)), gop, dq[md]);
+      }
     };
-    if (lo <= hi) copy(lo, Stage0{});
-    finish();
-    for (int jt = lo; jt <= hi; jt += 2) {
-      if (jt + 1 <= hi) copy(jt + 1, Stage1{});
-      tile(Stage0{});
-      finish();
-      if (jt + 1 > hi) break;
-      if (jt + 2 <= hi) copy(jt + 2, Stage0{});
-      tile(Stage1{});
-      finish();
+    wait_vm();  // the previous item's dQ stores: only this item's copies are counted below
+    if (t0 <= t1) {
+      copy(t0, std::integral_constant<int, 0>{});
+      if (t0 + 1 <= t1) copy(t0 + 1, std::integral_constant<int, 1>{});
+      if (t0 + 2 <= t1) copy(t0 + 2, std::integral_constant<int, 2>{});
     }
+    // the count of half tiles is even: groups of four, then at most one pair
+    int t = t0;
+    for (; t + 3 <= t1; t += 4) {
+      step(std::integral_constant<int, 0>{}, t);
+      step(std::integral_constant<int, 1>{}, t + 1);
+      step(std::integral_constant<int, 2>{}, t + 2);
+      step(std::integral_constant<int, 3>{}, t + 3);
+    }
+    if (t <= t1) {
+      step(std::integral_constant<int, 0>{}, t);
+      step(std::integral_constant<int, 1>{}, t + 1);
+    }
+    __syncthreads();  // every wave is done with the ring before the next item refills it
 
     const int qi = qt * 128 + qlane;
     if (qi < nq) {
