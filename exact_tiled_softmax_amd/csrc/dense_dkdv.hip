@@ -398,6 +398,28 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
       return as_vec8<E>(u32x4{x[4 * kh], x[4 * kh + 1], x[4 * kh + 2], x[4 * kh + 3]});
     };
 
+    // Stored gamma: block 0 of a step is written during B(0); block 1, whose
+    // gamma is complete only at the end of B(0), is kept (g1) and written
+    // during the first group of the next step (or by g1_flush), so that the
+    // vmcnt wait at the end of a step does not wait for stores issued just
+    // before it.
+    uint32_t g1[8];
+    bool g1_pend = false;
+    __amdgpu_buffer_rsrc_t g1_rs = make_rsrc(a.Gam, 0u);
+    uint32_t g1_soff = 0;
+    auto g1_store = [&](int u) __attribute__((always_inline)) {
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{g1[4 * u], g1[4 * u + 1], g1[4 * u + 2], g1[4 * u + 3]}, g1_rs,
+                                             gam_voff, g1_soff + (2 + u) * 1024, 0);
+    };
+    auto g1_flush = [&]() __attribute__((always_inline)) {
+      if constexpr (kGam) {
+        if (g1_pend) {
+          g1_store(0);
+          g1_store(1);
+        }
+        g1_pend = false;
+      }
+    };
     // one step on stage stg; its successor's rows go into the other stage
     auto step = [&](auto stg, int st, int sn, auto part_tag, bool cbm) __attribute__((always_inline)) {
       typedef std::integral_constant<int, 1 - decltype(stg)::value> Next;
@@ -443,12 +465,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
           }
           if constexpr (a_is_dp<KS>(u)) dp[mq] = E::mfma32(op, vreg[kk], dp[mq]);
           else sc[mq] = E::mfma32(op, kreg[kk], sc[mq]);
+          // the previous step's block 1
+          if constexpr (kGam && gi == 0 && (u == 2 || u == 5)) {
+            if (g1_pend) g1_store(u == 2 ? 0 : 1);
+          }
         } else {
           constexpr int kh = u / (2 * MD), md = (u % (2 * MD)) / 2;
           if constexpr (u & 1) dk[md] = E::mfma32(op, pack_op(w[mq].gw, kh), dk[md]);
           else dv[md] = E::mfma32(op, pack_op(w[mq].pw, kh), dv[md]);
           // stored gamma: the block's gamma (complete before B(mq)) to its image
-          if constexpr (kGam && u < 2) {
+          if constexpr (kGam && mq == 0 && u < 2) {
             if (gst)
               __builtin_amdgcn_raw_buffer_store_b128(
                   u32x4{w[mq].gw[4 * u], w[mq].gw[4 * u + 1], w[mq].gw[4 * u + 2], w[mq].gw[4 * u + 3]}, grs,
@@ -477,12 +503,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
         }
         ETS_FENCE();
       });
+      if constexpr (kGam) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) g1[k] = w[1].gw[k];
+        g1_pend = gst;
+        g1_rs = grs;
+        g1_soff = gsoff;
+      }
     };
     auto empty_step = [&](auto stg, int st, int sn) __attribute__((always_inline)) {
       typedef std::integral_constant<int, 1 - decltype(stg)::value> Next;
       copy_lse(sn, Next{});
 #pragma unroll
       for (int u = 0; u < NCOPY; ++u) copy_one(sn, Next{}, u);
+      g1_flush();
       if (gam_on) {  // no allowed pair: a zero block part where the dQ kernel reads one
         size_t lo;
         int qb0;
@@ -585,6 +619,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dense_bwd_dkdv_kernel(co
       }
     }
     general_until(1 << 30);
+    g1_flush();
 
     // ---- epilogue: dK = c dK^T, dV = (1/(1-rho)) dV^T; lane holds one key
     if (key < nk) {
