@@ -190,7 +190,9 @@ size_t attn_bwd_workspace_size_fast(attn_dtype dt, int B, int H, int H_kv, int n
  *   G         [B][H][n_q][dv] upstream gradient
  *   dQ, dK, dV  outputs shaped like Q, K, V
  *   workspace   device memory of at least attn_bwd_workspace_size() bytes,
- *               16-byte aligned; contents on entry are ignored
+ *               16-byte aligned; contents on entry are ignored.  With at
+ *               least attn_bwd_workspace_size_fast() bytes (dropout with a
+ *               causal / window mask) the stored-gamma form runs
  */
 attn_status attn_bwd(attn_dtype dt, int B, int H, int H_kv, int n_q, int n_k, int d, int dv,
                      const void* Q, const void* K, const void* V, const void* Y, const float* LSE,
