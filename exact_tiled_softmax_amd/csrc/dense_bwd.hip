@@ -22,7 +22,10 @@
 //         by LDS transpose reads.  No atomics.
 //   dq    query-major: the forward layout (queries along lanes); recomputes
 //         S^T and dP^T and accumulates dQ^T += K^T gamma^T, with K^T read by
-//         LDS transpose reads.  No atomics.
+//         LDS transpose reads.  No atomics.  With dropout and a causal /
+//         window mask, and a workspace large enough for them, dkdv also
+//         stores its gamma tiles and dq reads them instead of recomputing
+//         (dense_bwd_dq_stored_kernel in dense_dq.hip).
 #include "device.hpp"
 
 namespace ets {
